@@ -1,0 +1,226 @@
+/*
+ * MLA paged-KV decode oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU definition of what the decode path
+ * computes, used to judge the GPU library.  Only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg may load this file's library.  It shares
+ * no code, header, table or constant with the HIP library.
+ *
+ * All arithmetic is IEEE double.  bf16 and e4m3 inputs are widened exactly.
+ *
+ * What is computed (per request b, query row i < s_q, head h < h_q):
+ *   - Multi-head latent attention in its decode form: every query head attends
+ *     to one shared compressed latent row per cached token ("Was ist MLA?",
+ *     MHA/MQA/GQA/MLA table, Novita AI page: MQA-style sharing of one KV
+ *     stream by all query heads; MLA = latent vectors plus a decoupled RoPE
+ *     part).  Each token's key is 576 values: 512 latent + 64 RoPE.  The value
+ *     is the first 512 of them.
+ *   - The cache is paged in blocks of 64 tokens and reached through a
+ *     per-request block table (DeepSeek launch announcement quoted on the
+ *     8bitnewsroom FlashMLA page; feature list of the aivengo.media page).
+ *   - score_j = scale * <q, K_j>, lse = ln sum_j exp(score_j),
+ *     out = sum_j softmax_j * K_j[0:512]   (textbook softmax attention; the
+ *     pages never write the formula, this is the plain reading).
+ *   - Causal rows (s_q > 1): query row i is the (s_q-1-i)-th newest token and
+ *     sees the first L - (s_q - 1 - i) keys (bottom-right alignment).
+ *   - A row that sees no key returns out = 0 and lse = -inf.
+ *   - FP8 cache ("Key Contributions", DeepSeek KB page: 656 bytes per token,
+ *     RoPE slice kept in BF16): a token record is 512 OCP E4M3FN codes, then
+ *     four little-endian fp32 scales (one per 128-dim tile), then 64 bf16
+ *     RoPE values.  Dequantised key = e4m3(code) * scale[d / 128].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_D_QK = 576, ORC_D_V = 512, ORC_PAGE = 64 };
+enum { ORC_FP8_RECORD = 656, ORC_FP8_SCALES_AT = 512, ORC_FP8_ROPE_AT = 528 };
+
+/* bf16 is the top half of an IEEE binary32. */
+static double orc_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; subnormals when the exponent field is 0. */
+double mla_oracle_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* One cached token's 576-dim key, widened to double. */
+static void orc_key(const void *cache, int kind, int64_t phys, int slot, double *k)
+{
+    int d;
+    if (kind == 0) {
+        const uint16_t *row = (const uint16_t *)cache + (phys * ORC_PAGE + slot) * ORC_D_QK;
+        for (d = 0; d < ORC_D_QK; ++d)
+            k[d] = orc_bf16(row[d]);
+    } else {
+        const uint8_t *rec = (const uint8_t *)cache + (phys * ORC_PAGE + slot) * ORC_FP8_RECORD;
+        float scale[4];
+        memcpy(scale, rec + ORC_FP8_SCALES_AT, sizeof scale);
+        for (d = 0; d < ORC_D_V; ++d)
+            k[d] = mla_oracle_e4m3_value(rec[d]) * (double)scale[d / 128];
+        for (d = 0; d < ORC_D_QK - ORC_D_V; ++d) {
+            uint16_t bits;
+            memcpy(&bits, rec + ORC_FP8_ROPE_AT + 2 * d, 2);
+            k[ORC_D_V + d] = orc_bf16(bits);
+        }
+    }
+}
+
+/* Number of keys query row i of a request with L cached tokens may see. */
+static int64_t orc_visible(int64_t L, int s_q, int i, int causal)
+{
+    int64_t n = causal ? L - (int64_t)(s_q - 1 - i) : L;
+    if (n < 0) n = 0;
+    if (n > L) n = L;
+    return n;
+}
+
+/*
+ * Attention of one query row over keys [lo, hi) of its request (the window is
+ * further clipped to the keys the row may see).  out: 512 doubles.
+ */
+static void orc_attend(const uint16_t *q, int s_q, int h_q, const void *cache, int kind,
+                       const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
+                       double scale, int causal, int b, int i, int h, int64_t lo, int64_t hi,
+                       double *out, double *lse)
+{
+    double qd[ORC_D_QK], kd[ORC_D_QK];
+    const uint16_t *qrow = q + (((int64_t)b * s_q + i) * h_q + h) * ORC_D_QK;
+    int64_t n = orc_visible(seqlens[b], s_q, i, causal);
+    int64_t j, cnt;
+    double *score, mx, z;
+    int d;
+
+    if (lo < 0) lo = 0;
+    if (hi > n) hi = n;
+    for (d = 0; d < ORC_D_V; ++d)
+        out[d] = 0.0;
+    if (hi <= lo) {
+        *lse = -INFINITY;
+        return;
+    }
+    for (d = 0; d < ORC_D_QK; ++d)
+        qd[d] = orc_bf16(qrow[d]);
+
+    cnt = hi - lo;
+    score = (double *)malloc((size_t)cnt * sizeof(double));
+    mx = -INFINITY;
+    for (j = lo; j < hi; ++j) {
+        int64_t phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
+        double dot = 0.0;
+        orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
+        for (d = 0; d < ORC_D_QK; ++d)
+            dot += qd[d] * kd[d];
+        score[j - lo] = scale * dot;
+        if (score[j - lo] > mx) mx = score[j - lo];
+    }
+    z = 0.0;
+    for (j = lo; j < hi; ++j) {
+        int64_t phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
+        double w = exp(score[j - lo] - mx);
+        z += w;
+        orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
+        for (d = 0; d < ORC_D_V; ++d)
+            out[d] += w * kd[d];
+    }
+    for (d = 0; d < ORC_D_V; ++d)
+        out[d] /= z;
+    *lse = mx + log(z);
+    free(score);
+}
+
+/*
+ * Decode a list of query rows.
+ *   q            bf16 bits [batch, s_q, h_q, 576]
+ *   cache        kind 0: bf16 bits [num_pages, 64, 576];
+ *                kind 1: bytes [num_pages, 64, 656] (FP8 records)
+ *   block_table  int32 [batch, bt_stride]; logical block j of request b -> page
+ *   seqlens      int32 [batch]; cached tokens per request (including the s_q
+ *                tokens being decoded)
+ *   rows         int32 [n_rows, 3] = (b, i, h)
+ *   windows      NULL, or int64 [n_rows, 2] = key window [lo, hi) per row
+ *   out          double [n_rows, 512];  lse double [n_rows] (natural log)
+ * Returns the number of OpenMP threads used.
+ */
+int mla_oracle_decode_rows(const uint16_t *q, int s_q, int h_q, const void *cache, int kind,
+                           const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
+                           double scale, int causal, const int32_t *rows, int64_t n_rows,
+                           const int64_t *windows, double *out, double *lse)
+{
+    int threads = 1;
+    int64_t r;
+#ifdef _OPENMP
+    threads = omp_get_max_threads();
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < n_rows; ++r) {
+        int b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
+        int64_t lo = windows ? windows[2 * r] : 0;
+        int64_t hi = windows ? windows[2 * r + 1] : (int64_t)seqlens[b];
+        orc_attend(q, s_q, h_q, cache, kind, block_table, bt_stride, seqlens, scale, causal,
+                   b, i, h, lo, hi, out + r * ORC_D_V, lse + r);
+    }
+    return threads;
+}
+
+/*
+ * Merge attention results computed over disjoint key sets of the same row.
+ * Each part holds its own normalised output o_p and lse_p.  The merged lse is
+ * ln sum_p exp(lse_p) and the merged output weights each part by
+ * exp(lse_p - lse).  Parts with lse = -inf carry no keys and weigh 0.
+ *   o_parts [n_parts, dv], lse_parts [n_parts] -> out [dv], *lse
+ */
+void mla_oracle_lse_merge(const double *o_parts, const double *lse_parts, int n_parts, int dv,
+                          double *out, double *lse)
+{
+    double mx = -INFINITY, z = 0.0;
+    int p, d;
+    for (d = 0; d < dv; ++d)
+        out[d] = 0.0;
+    for (p = 0; p < n_parts; ++p)
+        if (lse_parts[p] > mx) mx = lse_parts[p];
+    if (mx == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    for (p = 0; p < n_parts; ++p)
+        z += exp(lse_parts[p] - mx);
+    *lse = mx + log(z);
+    for (p = 0; p < n_parts; ++p) {
+        double w = exp(lse_parts[p] - *lse);
+        if (lse_parts[p] == -INFINITY) continue;
+        for (d = 0; d < dv; ++d)
+            out[d] += w * o_parts[(int64_t)p * dv + d];
+    }
+}
+
+/* Dequantise one FP8 token record into 576 doubles (512 latent + 64 RoPE). */
+void mla_oracle_fp8_record_values(const uint8_t *record, double *k)
+{
+    orc_key(record, 1, 0, 0, k);
+}
+
+int mla_oracle_fp8_record_bytes(void) { return ORC_FP8_RECORD; }
+int mla_oracle_bf16_token_bytes(void) { return 2 * ORC_D_QK; }
