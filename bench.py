@@ -1,0 +1,219 @@
+"""Benchmark: MLA decode over a paged latent KV cache on one MI355X.
+
+One step = one pass of the whole decode path over one batch: the split-KV plan
+(mla_get_metadata), the attention kernel (mla_decode_attn) and the LSE
+combine (mla_decode_combine).  Inputs are resident in HBM before timing.
+
+The headline line is measured on the memory-bound workload (batch 128 x 4096
+tokens, h_q = 16); the same JSON line carries the other workloads
+(compute-bound h_q = 128, FP8 cache, long context) under "workloads", each
+with TFLOP/s, GB/s and roofline fractions, plus the oracle timed on the host
+cores as a CPU baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), h_q=16 and h_q=128"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="membound")
+    p.add_argument("--extra", default="computebound,fp8,longctx",
+                   help="comma list of further workloads to measure ('' for none)")
+    p.add_argument("--cpu-baseline", type=int, default=1)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+class Runner:
+    """Device inputs, a preallocated plan / workspace / outputs, and a step."""
+
+    def __init__(self, name):
+        import torch
+        import mla_paged_kv_fwd_amd as mla
+        import workloads as W
+
+        self.torch, self.mla, self.name = torch, mla, name
+        (self.q, self.kc, self.bt, self.sl, self.s_q, self.h_q, self.causal, self.scale,
+         self.fp8) = W.make_config_device(name)
+        seqlens = self.sl.cpu().numpy()
+        self.batch = seqlens.shape[0]
+        self.bytes = W.algorithmic_bytes(seqlens, self.s_q, self.h_q, self.fp8)
+        self.flops = W.algorithmic_flops(seqlens, self.s_q, self.h_q, self.causal)
+        self.num_parts = mla.default_num_parts(self.s_q, self.h_q)
+        dev = self.q.device
+        self.meta = torch.empty((self.num_parts, mla.META_INTS), dtype=torch.int32, device=dev)
+        self.split_base = torch.empty((self.batch + 1,), dtype=torch.int32, device=dev)
+        ws = mla.workspace_bytes(self.batch, self.s_q, self.h_q, self.num_parts)
+        self.ws = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((self.batch, self.s_q, self.h_q, mla.D_V), dtype=torch.bfloat16,
+                               device=dev)
+        self.lse = torch.empty((self.batch, self.s_q, self.h_q), dtype=torch.float32, device=dev)
+        lib = mla.lib()
+        self._plan_args = (self.sl.data_ptr(), self.batch, self.s_q, self.h_q, self.num_parts,
+                           self.meta.data_ptr(), self.split_base.data_ptr())
+        self._attn_args = (self.q.data_ptr(), self.kc.data_ptr(), 1 if self.fp8 else 0,
+                           self.kc.shape[0], self.bt.data_ptr(), self.bt.shape[1],
+                           self.sl.data_ptr(), self.batch, self.s_q, self.h_q, float(self.scale),
+                           int(self.causal), self.meta.data_ptr(), self.split_base.data_ptr(),
+                           self.num_parts, self.ws.data_ptr(), self.ws.numel(),
+                           self.out.data_ptr(), self.lse.data_ptr())
+        self._comb_args = (self.split_base.data_ptr(), self.batch, self.s_q, self.h_q,
+                           self.num_parts, self.ws.data_ptr(), self.ws.numel(),
+                           self.out.data_ptr(), self.lse.data_ptr())
+        self.lib = lib
+
+    def step(self, events=None):
+        stream = self.torch.cuda.current_stream()
+        s = stream.cuda_stream
+        if events is not None:
+            events[0].record(stream)
+        st = self.lib.mla_get_metadata(*self._plan_args, s)
+        if events is not None:
+            events[1].record(stream)
+        st |= self.lib.mla_decode_attn(*self._attn_args, s)
+        if events is not None:
+            events[2].record(stream)
+        st |= self.lib.mla_decode_combine(*self._comb_args, s)
+        if events is not None:
+            events[3].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libmla call failed in {self.name}")
+
+    def measure(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.step(evs[k])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / steps
+        plan = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+        attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+        comb = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+        n_split = int(self.split_base[-1].item())
+        return dict(ms_per_step=ms_step, plan_us=plan * 1e3, attn_us=attn * 1e3,
+                    combine_us=comb * 1e3, split_slots=n_split)
+
+    def report(self, m):
+        s = m["ms_per_step"] * 1e-3
+        a = m["attn_us"] * 1e-6
+        gbs, tfl = self.bytes / s / 1e9, self.flops / s / 1e12
+        gbs_k, tfl_k = self.bytes / a / 1e9, self.flops / a / 1e12
+        bound = "hbm" if self.bytes / (PEAK_HBM_GBS * 1e9) >= self.flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
+        return dict(
+            us_per_step=round(m["ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
+            attn_us=round(m["attn_us"], 2), combine_us=round(m["combine_us"], 2),
+            split_slots=m["split_slots"], num_parts=self.num_parts,
+            alg_bytes=self.bytes, alg_flops=self.flops,
+            gbs=round(gbs, 1), tflops=round(tfl, 1),
+            attn_gbs=round(gbs_k, 1), attn_tflops=round(tfl_k, 1),
+            hbm_frac=round(gbs / PEAK_HBM_GBS, 4), mfma_frac=round(tfl / PEAK_BF16_TFLOPS, 4),
+            bound=bound,
+            roofline_frac=round(max(gbs / PEAK_HBM_GBS, tfl / PEAK_BF16_TFLOPS), 4))
+
+
+def cpu_baseline(name, seconds):
+    """The oracle on a bounded sample of the workload: whole requests of the
+    same shape, doubling the sample until about `seconds` of wall time."""
+    import oracle
+    import workloads as W
+
+    cfg = W.CONFIGS[name]
+    rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
+    all_sl = W.config_seqlens(name, rng)
+    n = 1
+    while True:
+        sl = all_sl[:n]
+        case = W.make_case(sl, cfg["s_q"], cfg["h_q"], seed=cfg["seed"] + 1000, causal=cfg["causal"],
+                           fp8=cfg["fp8"])
+        rows = oracle.all_rows(case.batch, case.s_q, case.h_q)
+        t0 = time.perf_counter()
+        _, _, threads = oracle.decode_rows(case.q, case.cache, case.kind, case.block_table,
+                                           case.seqlens, case.scale, case.causal, rows)
+        dt = time.perf_counter() - t0
+        if dt >= seconds / 2 or n >= len(all_sl):
+            break
+        n = min(len(all_sl), n * 2)
+    b = W.algorithmic_bytes(sl, cfg["s_q"], cfg["h_q"], cfg["fp8"])
+    f = W.algorithmic_flops(sl, cfg["s_q"], cfg["h_q"], cfg["causal"])
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{n} of {len(all_sl)} requests ({cfg['desc']}), all rows, {dt:.2f} s",
+                tflops=round(f / dt / 1e12, 6), seconds=round(dt, 3))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    main_r = Runner(args.workload)
+    m = main_r.measure(args.steps, args.warmup)
+    rep = main_r.report(m)
+    print(f"[bench] {args.workload}: {json.dumps(rep)}", file=sys.stderr, flush=True)
+    workloads = {args.workload: rep}
+    del main_r
+    for name in [x for x in args.extra.split(",") if x]:
+        r = Runner(name)
+        rep_x = r.report(r.measure(args.steps, args.warmup))
+        print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
+        workloads[name] = rep_x
+        del r
+        torch.cuda.empty_cache()
+    head = workloads[args.workload]
+    attn_gbs = head["attn_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": head["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {W.CONFIGS[args.workload]['desc']}, page 64",
+                   "batch": int(len(W.CONFIGS[args.workload]['seqlens'])) if not isinstance(
+                       W.CONFIGS[args.workload]['seqlens'], tuple) else 64,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_rowgroup_kernel<false>"},
+        "workloads": workloads,
+    }
+    if args.cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

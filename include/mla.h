@@ -1,0 +1,180 @@
+/*
+ * libmla -- Multi-head Latent Attention decode over a paged latent KV cache,
+ * for AMD MI355X (gfx950).
+ *
+ * What is computed.  For each request b (cached length L_b), each of its s_q
+ * new query tokens i and each of h_q query heads h, one attention row:
+ *     score_j = softmax_scale * <q[b,i,h,0:576], K_j[0:576]>,  j < n(b,i)
+ *     lse     = ln sum_j exp(score_j)
+ *     out     = sum_j exp(score_j - lse) * K_j[0:512]
+ * Every head shares the same cached latent row K_j per token: the MQA-style
+ * sharing of one KV stream that MLA uses, with a 512-dim compressed latent
+ * plus a 64-dim decoupled RoPE part (Novita AI FlashMLA page, section
+ * "Was ist MLA?", MHA/MQA/GQA/MLA comparison table).  The value is the first
+ * 512 dims of the same row.  n(b,i) = L_b without causal masking; with causal
+ * masking row i is the (s_q-1-i)-th newest token and sees L_b - (s_q-1-i)
+ * keys.  A row that sees no key gets out = 0, lse = -inf.
+ *
+ * Cache layouts (both paged in blocks of 64 tokens: DeepSeek launch
+ * announcement on the 8bitnewsroom FlashMLA page; aivengo.media feature list):
+ *   bf16: [num_pages][64][576] bf16, 1152 bytes per token.
+ *   fp8 : [num_pages][64][656] bytes, one 656-byte record per token
+ *         (DeepSeek KB page, "Key Contributions": 656 vs 1152 bytes per
+ *         token, RoPE slice kept in BF16): bytes [0,512) OCP E4M3FN codes of
+ *         latent dims 0..511; [512,528) four little-endian fp32 scales, one per
+ *         128-dim tile (value = code * scale); [528,656) 64 bf16 RoPE dims.
+ * block_table[b * block_table_stride + j] is the physical page holding
+ * tokens [64 j, 64 j + 64) of request b.  Only entries j < ceil(L_b / 64) are
+ * read; cache slots at or beyond L_b are never read.
+ *
+ * Conventions.
+ *   - Pointers are device pointers unless a name ends in _host.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every device
+ *     call only enqueues work on it and returns; nothing synchronises.
+ *   - The caller owns every buffer.  The library allocates and frees nothing
+ *     and keeps no state besides a per-device cache of the CU count.
+ *   - Tensors are dense and row-major:
+ *       q     bf16  [batch][s_q][h_q][576]
+ *       out   bf16  [batch][s_q][h_q][512]
+ *       lse   fp32  [batch][s_q][h_q]      (natural log)
+ *       seqlens int32 [batch]; block_table int32 [batch][block_table_stride]
+ *   - Shapes supported: s_q in {1, 2}; h_q in {16, 32, 64, 128}; one shared
+ *     KV head; d_qk 576, d_v 512, page 64.  Others: MLA_ERR_UNSUPPORTED.
+ *   - Argument errors that the host can see are reported before any HIP call.
+ *     Device-resident contents (page ids inside [0, num_pages), lengths that
+ *     fit the block table) are the caller's contract and are not checked.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad stride */
+    MLA_ERR_UNSUPPORTED = -2, /* shape outside the supported set */
+    MLA_ERR_WORKSPACE = -3,   /* workspace smaller than mla_workspace_bytes */
+    MLA_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+} mla_status;
+
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_PAGE 64
+#define MLA_FP8_RECORD 656
+#define MLA_META_INTS 8
+#define MLA_MAX_BATCH 32768
+#define MLA_MAX_PARTS 16384
+
+/* Static string for a status code.  Thread-safe; never NULL. */
+const char *mla_status_string(int status);
+
+/* Number of int32 in the plan buffer `meta` for num_parts parts. */
+size_t mla_metadata_ints(int num_parts);
+
+/* Bytes of split workspace needed by mla_decode_* for these sizes (the upper
+ * bound over every plan with num_parts parts: at most batch + num_parts
+ * request segments, each holding s_q*h_q rows of 512 fp32 + 1 fp32 lse). */
+size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
+
+/* Overhead, in page units, that the planner charges per request segment:
+ * 1 + (s_q * h_q) / 64. */
+int mla_plan_overhead(int s_q, int h_q);
+
+/* Plan size suited to the kernels on `device` (a multiple of 8 derived from
+ * the CU count); < 0 on error (status code).  Needs a visible GPU. */
+int mla_default_num_parts(int device, int s_q, int h_q);
+
+/*
+ * Split-KV plan.  Cuts the batch's pages into num_parts contiguous pieces of
+ * equal cost so that every CU gets the same amount of work however the
+ * lengths vary (the launch announcement quoted on the 8bitnewsroom FlashMLA
+ * page says the kernel targets variable-length batches; the cut rule is this
+ * library's).  Definition: request b has n_b = ceil(L_b/64) pages; requests
+ * with pages are laid end to end on a cost line, each taking
+ * c = mla_plan_overhead(s_q, h_q) units then one unit per page, total T.
+ * With P = min(num_parts, T), the page at cost position x goes to part
+ * floor(x * P / T).
+ *   seqlens    int32 [batch] (device)
+ *   meta       int32 [num_parts][8] (device, written): for a part with pages
+ *              {b_first, j_first, b_last, j_last, split_first, 0, 0, 0} --
+ *              it runs from page j_first of request b_first to page j_last of
+ *              b_last inclusive; split_first is its rank among the parts that
+ *              touch b_first.  A part without pages has b_first = -1.
+ *   split_base int32 [batch + 1] (device, written): prefix sum of the number
+ *              of parts touching each request; request b owns workspace split
+ *              slots [split_base[b], split_base[b+1]).
+ * One small kernel on `stream`; no host synchronisation.
+ */
+mla_status mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,
+                            int32_t *meta, int32_t *split_base, void *stream);
+
+/* The same plan computed on the host from host arrays (no GPU needed). */
+mla_status mla_get_metadata_host(const int32_t *seqlens_host, int batch, int s_q, int h_q,
+                                 int num_parts, int32_t *meta_host, int32_t *split_base_host);
+
+/*
+ * bf16-cache decode: attention kernel plus, for requests the plan split, the
+ * LSE merge of their partial results (mla_decode_attn then mla_decode_combine).
+ *   q           bf16 [batch][s_q][h_q][576]
+ *   kcache      bf16 [num_pages][64][576]
+ *   block_table int32 [batch][block_table_stride]
+ *   seqlens     int32 [batch]
+ *   softmax_scale  multiplies the full 576-dim dot product
+ *   causal      0 or 1 (only matters for s_q > 1)
+ *   meta, split_base, num_parts   a plan from mla_get_metadata for the same
+ *               seqlens, s_q, h_q
+ *   workspace   >= mla_workspace_bytes(batch, s_q, h_q, num_parts) bytes,
+ *               256-byte aligned; scratch owned by the caller
+ *   out         bf16 [batch][s_q][h_q][512];  lse  fp32 [batch][s_q][h_q]
+ */
+mla_status mla_decode_fwd(const void *q, const void *kcache, int64_t num_pages,
+                          const int32_t *block_table, int block_table_stride,
+                          const int32_t *seqlens, int batch, int s_q, int h_q,
+                          float softmax_scale, int causal, const int32_t *meta,
+                          const int32_t *split_base, int num_parts, void *workspace,
+                          size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/* FP8-cache decode: as mla_decode_fwd with kcache_fp8 = uint8
+ * [num_pages][64][656] records (E4M3FN codes dequantised in the kernel). */
+mla_status mla_decode_fwd_fp8(const void *q, const void *kcache_fp8, int64_t num_pages,
+                              const int32_t *block_table, int block_table_stride,
+                              const int32_t *seqlens, int batch, int s_q, int h_q,
+                              float softmax_scale, int causal, const int32_t *meta,
+                              const int32_t *split_base, int num_parts, void *workspace,
+                              size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * First half of mla_decode_fwd{,_fp8}: the attention kernel alone.  Writes
+ * out/lse for requests the plan did not split and partial results
+ * (normalised fp32 output + lse per split slot) into the workspace for the
+ * others.  kv_format: 0 = bf16 cache, 1 = fp8 records.  Arguments as above.
+ */
+mla_status mla_decode_attn(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                           const int32_t *block_table, int block_table_stride,
+                           const int32_t *seqlens, int batch, int s_q, int h_q,
+                           float softmax_scale, int causal, const int32_t *meta,
+                           const int32_t *split_base, int num_parts, void *workspace,
+                           size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * Second half: for every request with two or more split slots, merges the
+ * slots' partial results by their log-sum-exp (merged lse = ln sum_s
+ * exp(lse_s); out = sum_s exp(lse_s - lse) * o_s) and writes out/lse.
+ * Requests with no pages get out = 0, lse = -inf.  Requests with one slot
+ * are left as mla_decode_attn wrote them.  Workspace layout: o fp32
+ * [batch + num_parts][s_q*h_q][512], then lse fp32 [batch + num_parts][s_q*h_q].
+ */
+mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int h_q,
+                              int num_parts, const void *workspace, size_t workspace_bytes,
+                              void *out, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

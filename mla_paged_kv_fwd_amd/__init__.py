@@ -1,0 +1,205 @@
+"""Python binding of libmla: MLA decode over a paged latent KV cache on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/mla.h``: every
+step of the computation runs in the library's HIP kernels.  PyTorch provides
+device memory and the current stream only.  If ``libmla.so`` has not been
+built, every call raises; there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MlaError", "lib", "D_QK", "D_V", "PAGE", "FP8_RECORD", "META_INTS",
+    "default_num_parts", "plan_overhead", "workspace_bytes", "get_metadata",
+    "get_metadata_host", "decode", "decode_attn", "decode_combine", "status_string",
+]
+
+D_QK = 576
+D_V = 512
+PAGE = 64
+FP8_RECORD = 656
+META_INTS = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "mla_status_string": (ctypes.c_char_p, [_I]),
+    "mla_metadata_ints": (_SZ, [_I]),
+    "mla_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "mla_plan_overhead": (_I, [_I, _I]),
+    "mla_default_num_parts": (_I, [_I, _I, _I]),
+    "mla_get_metadata": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "mla_get_metadata_host": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "mla_decode_fwd": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
+                            _P, _P, _P]),
+    "mla_decode_fwd_fp8": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P,
+                                _SZ, _P, _P, _P]),
+    "mla_decode_attn": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P,
+                             _SZ, _P, _P, _P]),
+    "mla_decode_combine": (_I, [_P, _I, _I, _I, _I, _P, _SZ, _P, _P, _P]),
+}
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libmla.so (built in-tree by ``mla_paged_kv_fwd_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MlaError(f"{LIB_PATH} is not built; run `python -m mla_paged_kv_fwd_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().mla_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise MlaError(f"{what}: {status_string(status)} ({status})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def plan_overhead(s_q, h_q):
+    return lib().mla_plan_overhead(s_q, h_q)
+
+
+def workspace_bytes(batch, s_q, h_q, num_parts):
+    return lib().mla_workspace_bytes(batch, s_q, h_q, num_parts)
+
+
+def default_num_parts(s_q, h_q, device=None):
+    dev = torch.cuda.current_device() if device is None else int(device)
+    n = lib().mla_default_num_parts(dev, s_q, h_q)
+    if n < 0:
+        _check(n, "mla_default_num_parts")
+    return n
+
+
+def get_metadata(seqlens, s_q, h_q, num_parts=None):
+    """Plan split-KV work on the GPU.  seqlens: int32 CUDA tensor [batch].
+
+    Returns (meta int32 [num_parts, 8], split_base int32 [batch + 1], num_parts).
+    """
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
+        raise MlaError("seqlens must be a contiguous int32 CUDA tensor")
+    if num_parts is None:
+        num_parts = default_num_parts(s_q, h_q, seqlens.device.index)
+    batch = seqlens.shape[0]
+    meta = torch.empty((num_parts, META_INTS), dtype=torch.int32, device=seqlens.device)
+    split_base = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
+    _check(lib().mla_get_metadata(_ptr(seqlens), batch, s_q, h_q, num_parts, _ptr(meta),
+                                  _ptr(split_base), _stream()), "mla_get_metadata")
+    return meta, split_base, num_parts
+
+
+def get_metadata_host(seqlens, s_q, h_q, num_parts):
+    """Host twin of get_metadata on CPU int32 tensors (no GPU needed)."""
+    sl = torch.as_tensor(seqlens, dtype=torch.int32).contiguous()
+    batch = sl.shape[0]
+    meta = torch.empty((num_parts, META_INTS), dtype=torch.int32)
+    split_base = torch.empty((batch + 1,), dtype=torch.int32)
+    _check(lib().mla_get_metadata_host(_ptr(sl), batch, s_q, h_q, num_parts, _ptr(meta),
+                                       _ptr(split_base)), "mla_get_metadata_host")
+    return meta, split_base
+
+
+def _validate(q, kcache, block_table, seqlens, fp8):
+    if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != D_QK:
+        raise MlaError("q must be bf16 [batch, s_q, h_q, 576]")
+    if fp8:
+        if kcache.dtype != torch.uint8 or tuple(kcache.shape[1:]) != (PAGE, FP8_RECORD):
+            raise MlaError("fp8 kcache must be uint8 [pages, 64, 656]")
+    else:
+        if kcache.dtype != torch.bfloat16 or tuple(kcache.shape[1:]) != (PAGE, D_QK):
+            raise MlaError("kcache must be bf16 [pages, 64, 576]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise MlaError("block_table must be int32 [batch, width]")
+    if seqlens.dtype != torch.int32 or seqlens.dim() != 1:
+        raise MlaError("seqlens must be int32 [batch]")
+    for t in (q, kcache, block_table, seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise MlaError("all tensors must be contiguous CUDA tensors")
+
+
+def _outputs(q, out, lse):
+    b, s_q, h_q, _ = q.shape
+    if out is None:
+        out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _workspace(q, num_parts, workspace):
+    b, s_q, h_q, _ = q.shape
+    need = workspace_bytes(b, s_q, h_q, num_parts)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def decode_attn(q, kcache, block_table, seqlens, softmax_scale, causal, meta, split_base,
+                num_parts, workspace, out=None, lse=None, fp8=False):
+    """Attention kernel only (the first half of decode)."""
+    _validate(q, kcache, block_table, seqlens, fp8)
+    out, lse = _outputs(q, out, lse)
+    b, s_q, h_q, _ = q.shape
+    _check(lib().mla_decode_attn(
+        _ptr(q), _ptr(kcache), 1 if fp8 else 0, kcache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seqlens), b, s_q, h_q, float(softmax_scale), int(bool(causal)),
+        _ptr(meta), _ptr(split_base), num_parts, _ptr(workspace), workspace.numel(), _ptr(out),
+        _ptr(lse), _stream()), "mla_decode_attn")
+    return out, lse
+
+
+def decode_combine(split_base, num_parts, workspace, out, lse):
+    """LSE merge of split partials (the second half of decode)."""
+    b, s_q, h_q, _ = out.shape
+    _check(lib().mla_decode_combine(_ptr(split_base), b, s_q, h_q, num_parts, _ptr(workspace),
+                                    workspace.numel(), _ptr(out), _ptr(lse), _stream()),
+           "mla_decode_combine")
+    return out, lse
+
+
+def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, split_base=None,
+           num_parts=None, workspace=None, out=None, lse=None, fp8=False):
+    """MLA decode: returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q])."""
+    _validate(q, kcache, block_table, seqlens, fp8)
+    b, s_q, h_q, _ = q.shape
+    if meta is None:
+        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts)
+    out, lse = _outputs(q, out, lse)
+    workspace = _workspace(q, num_parts, workspace)
+    fn = lib().mla_decode_fwd_fp8 if fp8 else lib().mla_decode_fwd
+    _check(fn(_ptr(q), _ptr(kcache), kcache.shape[0], _ptr(block_table), block_table.shape[1],
+              _ptr(seqlens), b, s_q, h_q, float(softmax_scale), int(bool(causal)), _ptr(meta),
+              _ptr(split_base), num_parts, _ptr(workspace), workspace.numel(), _ptr(out),
+              _ptr(lse), _stream()), "mla_decode_fwd")
+    return out, lse

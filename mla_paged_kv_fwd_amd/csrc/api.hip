@@ -1,0 +1,221 @@
+// libmla C ABI: argument validation and launches.  Every host-visible error is
+// reported before the first HIP call.
+#include <math.h>
+
+#include "../../include/mla.h"
+#include "common.h"
+
+namespace mla {
+hipError_t launch_plan(const int32_t *seqlens, int batch, int c, int num_parts, int32_t *meta,
+                       int32_t *split_base, hipStream_t stream);
+void plan_host(const int32_t *seqlens, int batch, int c, int num_parts, int32_t *meta,
+               int32_t *split_base);
+hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
+int decode_rows_per_group();
+hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
+                          const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
+}  // namespace mla
+
+static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::kPage &&
+                  MLA_FP8_RECORD == mla::kTokBytesFp8 && MLA_META_INTS == mla::kMetaInts,
+              "header and kernels disagree");
+
+namespace {
+
+bool shape_supported(int s_q, int h_q) {
+    return (s_q == 1 || s_q == 2) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
+}
+
+mla_status check_plan_args(int batch, int s_q, int h_q, int num_parts) {
+    if (batch <= 0 || num_parts <= 0 || s_q <= 0 || h_q <= 0) return MLA_ERR_INVALID_ARG;
+    if (batch > mla::kMaxBatch || num_parts > mla::kMaxParts) return MLA_ERR_UNSUPPORTED;
+    if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+size_t workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
+    const size_t slots = (size_t)batch + (size_t)num_parts;
+    const size_t rows = (size_t)s_q * h_q;
+    return slots * rows * (mla::kDV + 1) * sizeof(float);
+}
+
+mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                            const int32_t *block_table, int block_table_stride,
+                            const int32_t *seqlens, int batch, int s_q, int h_q,
+                            float softmax_scale, int causal, const int32_t *meta,
+                            const int32_t *split_base, int num_parts, void *workspace,
+                            size_t ws_bytes, void *out, float *lse, void *stream) {
+    if (!q || !kcache || !block_table || !seqlens || !meta || !split_base || !out || !lse)
+        return MLA_ERR_INVALID_ARG;
+    if (kv_format != 0 && kv_format != 1) return MLA_ERR_INVALID_ARG;
+    if (num_pages <= 0 || block_table_stride < 1) return MLA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    mla_status st = check_plan_args(batch, s_q, h_q, num_parts);
+    if (st != MLA_OK) return st;
+    if (!workspace) return MLA_ERR_WORKSPACE;
+    if (ws_bytes < workspace_bytes(batch, s_q, h_q, num_parts)) return MLA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_WORKSPACE;
+
+    mla::DecodeArgs a;
+    const int M = s_q * h_q;
+    const size_t slots = (size_t)batch + num_parts;
+    a.q = (const uint16_t *)q;
+    a.kv = (const unsigned char *)kcache;
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.meta = meta;
+    a.split_base = split_base;
+    a.o_part = (float *)workspace;
+    a.lse_part = (float *)workspace + slots * M * mla::kDV;
+    a.out = (uint16_t *)out;
+    a.lse = lse;
+    a.bt_stride = block_table_stride;
+    a.batch = batch;
+    a.s_q = s_q;
+    a.h_q = h_q;
+    a.M = M;
+    a.num_parts = num_parts;
+    a.row_groups = M / mla::decode_rows_per_group();
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.causal = causal;
+    hipError_t e = mla::launch_decode(a, kv_format == 1, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status combine_impl(const int32_t *split_base, int batch, int s_q, int h_q, int num_parts,
+                        const void *workspace, size_t ws_bytes, void *out, float *lse,
+                        void *stream) {
+    if (!split_base || !out || !lse) return MLA_ERR_INVALID_ARG;
+    mla_status st = check_plan_args(batch, s_q, h_q, num_parts);
+    if (st != MLA_OK) return st;
+    if (!workspace || ws_bytes < workspace_bytes(batch, s_q, h_q, num_parts))
+        return MLA_ERR_WORKSPACE;
+    const int M = s_q * h_q;
+    const size_t slots = (size_t)batch + num_parts;
+    const float *o_part = (const float *)workspace;
+    const float *lse_part = o_part + slots * M * mla::kDV;
+    hipError_t e = mla::launch_combine(split_base, batch, M, o_part, lse_part, (uint16_t *)out,
+                                       lse, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int g_cu_count[64];
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_status_string(int status) {
+    switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MLA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t mla_metadata_ints(int num_parts) {
+    return num_parts > 0 ? (size_t)num_parts * mla::kMetaInts : 0;
+}
+
+size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
+    if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0) return 0;
+    return workspace_bytes(batch, s_q, h_q, num_parts);
+}
+
+int mla_plan_overhead(int s_q, int h_q) { return mla::plan_overhead(s_q, h_q); }
+
+int mla_default_num_parts(int device, int s_q, int h_q) {
+    if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+    if (device < 0 || device >= 64) return MLA_ERR_INVALID_ARG;
+    if (g_cu_count[device] <= 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            cus <= 0)
+            return MLA_ERR_HIP;
+        g_cu_count[device] = cus;
+    }
+    // one work-group of the row-group kernel per CU and part
+    int parts = g_cu_count[device];
+    return (parts + 7) / 8 * 8;
+}
+
+mla_status mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,
+                            int32_t *meta, int32_t *split_base, void *stream) {
+    if (!seqlens || !meta || !split_base) return MLA_ERR_INVALID_ARG;
+    mla_status st = check_plan_args(batch, s_q, h_q, num_parts);
+    if (st != MLA_OK) return st;
+    hipError_t e = mla::launch_plan(seqlens, batch, mla::plan_overhead(s_q, h_q), num_parts, meta,
+                                    split_base, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_get_metadata_host(const int32_t *seqlens_host, int batch, int s_q, int h_q,
+                                 int num_parts, int32_t *meta_host, int32_t *split_base_host) {
+    if (!seqlens_host || !meta_host || !split_base_host) return MLA_ERR_INVALID_ARG;
+    mla_status st = check_plan_args(batch, s_q, h_q, num_parts);
+    if (st != MLA_OK) return st;
+    mla::plan_host(seqlens_host, batch, mla::plan_overhead(s_q, h_q), num_parts, meta_host,
+                   split_base_host);
+    return MLA_OK;
+}
+
+mla_status mla_decode_attn(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                           const int32_t *block_table, int block_table_stride,
+                           const int32_t *seqlens, int batch, int s_q, int h_q,
+                           float softmax_scale, int causal, const int32_t *meta,
+                           const int32_t *split_base, int num_parts, void *workspace,
+                           size_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return decode_attn_impl(q, kcache, kv_format, num_pages, block_table, block_table_stride,
+                            seqlens, batch, s_q, h_q, softmax_scale, causal, meta, split_base,
+                            num_parts, workspace, workspace_bytes_, out, lse, stream);
+}
+
+mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int h_q,
+                              int num_parts, const void *workspace, size_t workspace_bytes_,
+                              void *out, float *lse, void *stream) {
+    return combine_impl(split_base, batch, s_q, h_q, num_parts, workspace, workspace_bytes_, out,
+                        lse, stream);
+}
+
+static mla_status decode_fwd(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                             const int32_t *block_table, int block_table_stride,
+                             const int32_t *seqlens, int batch, int s_q, int h_q,
+                             float softmax_scale, int causal, const int32_t *meta,
+                             const int32_t *split_base, int num_parts, void *workspace,
+                             size_t ws_bytes, void *out, float *lse, void *stream) {
+    mla_status st = decode_attn_impl(q, kcache, kv_format, num_pages, block_table,
+                                     block_table_stride, seqlens, batch, s_q, h_q, softmax_scale,
+                                     causal, meta, split_base, num_parts, workspace, ws_bytes, out,
+                                     lse, stream);
+    if (st != MLA_OK) return st;
+    return combine_impl(split_base, batch, s_q, h_q, num_parts, workspace, ws_bytes, out, lse,
+                        stream);
+}
+
+mla_status mla_decode_fwd(const void *q, const void *kcache, int64_t num_pages,
+                          const int32_t *block_table, int block_table_stride,
+                          const int32_t *seqlens, int batch, int s_q, int h_q,
+                          float softmax_scale, int causal, const int32_t *meta,
+                          const int32_t *split_base, int num_parts, void *workspace,
+                          size_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return decode_fwd(q, kcache, 0, num_pages, block_table, block_table_stride, seqlens, batch,
+                      s_q, h_q, softmax_scale, causal, meta, split_base, num_parts, workspace,
+                      workspace_bytes_, out, lse, stream);
+}
+
+mla_status mla_decode_fwd_fp8(const void *q, const void *kcache_fp8, int64_t num_pages,
+                              const int32_t *block_table, int block_table_stride,
+                              const int32_t *seqlens, int batch, int s_q, int h_q,
+                              float softmax_scale, int causal, const int32_t *meta,
+                              const int32_t *split_base, int num_parts, void *workspace,
+                              size_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return decode_fwd(q, kcache_fp8, 1, num_pages, block_table, block_table_stride, seqlens, batch,
+                      s_q, h_q, softmax_scale, causal, meta, split_base, num_parts, workspace,
+                      workspace_bytes_, out, lse, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+"""CPU checks of the C ABI: exports, status codes, host-side validation and the
+planner's host twin against the oracle plan.  No GPU call is made: every
+argument error is reported before the library touches HIP."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.libmla_loader import load_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = load_lib()
+    names = _declared_functions()
+    assert "mla_decode_fwd" in names and "mla_get_metadata" in names and "mla_decode_fwd_fp8" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = load_lib()
+    lib.mla_status_string.restype = ctypes.c_char_p
+    for code in (0, -1, -2, -3, -4, 7):
+        s = lib.mla_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_sizes_and_overhead():
+    lib = load_lib()
+    lib.mla_workspace_bytes.restype = ctypes.c_size_t
+    lib.mla_metadata_ints.restype = ctypes.c_size_t
+    assert lib.mla_metadata_ints(256) == 256 * 8
+    assert lib.mla_workspace_bytes(128, 1, 16, 256) == (128 + 256) * 16 * 513 * 4
+    assert lib.mla_workspace_bytes(0, 1, 16, 256) == 0
+    for s_q in (1, 2):
+        for h_q in (16, 32, 64, 128):
+            assert lib.mla_plan_overhead(s_q, h_q) == oracle.plan_overhead(s_q, h_q)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _decode(lib, **kw):
+    args = dict(q=FAKE, kc=FAKE, num_pages=10, bt=FAKE, stride=4, sl=FAKE, batch=2, s_q=1, h_q=16,
+                scale=0.04, causal=0, meta=FAKE, sb=FAKE, parts=8, ws=ctypes.c_void_p(0x10000),
+                ws_bytes=1 << 30, out=FAKE, lse=FAKE)
+    args.update(kw)
+    fn = lib.mla_decode_fwd
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    return fn(args["q"], args["kc"], args["num_pages"], args["bt"], args["stride"], args["sl"],
+              args["batch"], args["s_q"], args["h_q"], args["scale"], args["causal"], args["meta"],
+              args["sb"], args["parts"], args["ws"], args["ws_bytes"], args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID),
+    (dict(kc=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(batch=0), INVALID),
+    (dict(num_pages=0), INVALID),
+    (dict(stride=0), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(h_q=8), UNSUPPORTED),
+    (dict(h_q=48), UNSUPPORTED),
+    (dict(s_q=3), UNSUPPORTED),
+    (dict(batch=100000), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=1000), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), WORKSPACE),
+])
+def test_argument_errors_are_reported_before_any_gpu_call(kw, expect):
+    assert _decode(load_lib(), **kw) == expect
+
+
+def test_metadata_argument_errors():
+    lib = load_lib()
+    fn = lib.mla_get_metadata
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert fn(None, 2, 1, 16, 8, FAKE, FAKE, None) == INVALID
+    assert fn(FAKE, 2, 1, 16, 0, FAKE, FAKE, None) == INVALID
+    assert fn(FAKE, 2, 1, 12, 8, FAKE, FAKE, None) == UNSUPPORTED
+    assert fn(FAKE, 2, 1, 16, 100000, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def _host_plan(lib, seqlens, s_q, h_q, parts):
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    meta = np.full((parts, 8), 12345, dtype=np.int32)
+    sb = np.full((len(sl) + 1,), 12345, dtype=np.int32)
+    fn = lib.mla_get_metadata_host
+    fn.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    st = fn(sl.ctypes.data, len(sl), s_q, h_q, parts, meta.ctypes.data, sb.ctypes.data)
+    assert st == OK
+    return meta, sb
+
+
+PLAN_CASES = [
+    ([37, 100], 1, 16, 8),
+    ([4096] * 128, 1, 16, 256),
+    ([131072] * 8, 1, 128, 256),
+    ([0, 5, 0, 0, 64, 65, 0], 2, 32, 7),
+    ([1], 1, 16, 1024),
+    ([0, 0, 0], 1, 16, 8),
+    ([7] * 300, 2, 64, 16),
+    ([16384] * 64, 1, 128, 256),
+]
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,parts", PLAN_CASES)
+def test_host_planner_equals_oracle_plan(seqlens, s_q, h_q, parts):
+    meta, sb = _host_plan(load_lib(), seqlens, s_q, h_q, parts)
+    ref_meta, ref_sb = oracle.plan(seqlens, parts, oracle.plan_overhead(s_q, h_q))
+    np.testing.assert_array_equal(meta, np.array(ref_meta, dtype=np.int32))
+    np.testing.assert_array_equal(sb, np.array(ref_sb, dtype=np.int32))
+
+
+def test_host_planner_random_batches_equal_oracle():
+    rng = np.random.default_rng(7)
+    lib = load_lib()
+    for _ in range(60):
+        batch = int(rng.integers(1, 40))
+        seqlens = rng.integers(0, 3000, size=batch)
+        seqlens[rng.random(batch) < 0.2] = 0
+        parts = int(rng.integers(1, 300))
+        s_q, h_q = int(rng.choice([1, 2])), int(rng.choice([16, 32, 64, 128]))
+        meta, sb = _host_plan(lib, seqlens, s_q, h_q, parts)
+        ref_meta, ref_sb = oracle.plan(list(seqlens), parts, oracle.plan_overhead(s_q, h_q))
+        np.testing.assert_array_equal(meta, np.array(ref_meta, dtype=np.int32))
+        np.testing.assert_array_equal(sb, np.array(ref_sb, dtype=np.int32))

@@ -1,0 +1,116 @@
+"""GPU parity: libmla (through its C ABI) against the fp64 CPU oracle on the
+same seeded inputs.  Small cases compare every output; the full-size workloads
+compare a deterministic sample of rows the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import compare, oracle_all, run_gpu, sample_rows, to_device
+from tests.libmla_loader import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def test_tiny_workload_matches_oracle():
+    case = W.make_config("tiny")
+    out, lse = run_gpu(case)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, "tiny")
+
+
+SHAPES = [
+    # seqlens, s_q, h_q, causal, fp8
+    ([1, 63, 64, 65, 127, 128, 200, 1000], 1, 16, False, False),
+    ([1, 63, 64, 65, 127, 128, 200, 1000], 2, 16, True, False),
+    ([2, 64, 129, 700], 1, 32, False, False),
+    ([2, 65, 300], 2, 32, True, False),
+    ([3, 64, 190, 513], 1, 64, False, False),
+    ([5, 64, 257], 1, 128, False, False),
+    ([2, 66, 130, 400], 2, 128, True, False),
+    ([1, 63, 64, 65, 200, 1000], 1, 16, False, True),
+    ([2, 65, 300], 2, 32, True, True),
+    ([5, 64, 257], 1, 128, False, True),
+]
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal,fp8", SHAPES)
+def test_shapes_with_poisoned_tails_match_oracle(seqlens, s_q, h_q, causal, fp8):
+    case = W.make_case(seqlens, s_q, h_q, seed=100 + h_q + s_q, causal=causal, fp8=fp8,
+                       spare_pages=3, poison=True)
+    out, lse = run_gpu(case)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, f"{seqlens} s_q={s_q} h_q={h_q} causal={causal} fp8={fp8}")
+
+
+@pytest.mark.parametrize("num_parts", [1, 7, 64, 256, 1024])
+def test_result_does_not_depend_on_the_split(num_parts):
+    case = W.make_case([900, 33, 2000, 64], 2, 32, seed=7, causal=True, spare_pages=2, poison=True)
+    out, lse = run_gpu(case, num_parts=num_parts)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, f"num_parts={num_parts}")
+
+
+def test_empty_requests_and_empty_causal_rows():
+    # L = 0 requests, and L = 1 under s_q = 2 causal (row 0 sees no key)
+    case = W.make_case([0, 1, 70, 0, 1], 2, 16, seed=8, causal=True, spare_pages=1, poison=True)
+    out, lse = run_gpu(case, num_parts=8)
+    ref_out, ref_lse = oracle_all(case)
+    assert np.isneginf(ref_lse[0]).all() and np.isneginf(ref_lse[1, 0]).all()
+    compare(out, lse, ref_out, ref_lse, "empty rows")
+
+
+def test_gpu_plan_equals_oracle_plan():
+    import mla_paged_kv_fwd_amd as mla
+
+    rng = np.random.default_rng(3)
+    cases = [([37, 100], 1, 16, 8), ([4096] * 128, 1, 16, 256), ([131072] * 8, 1, 128, 256),
+             ([0, 5, 0, 0, 64, 65, 0], 2, 32, 7), ([1], 1, 16, 1024), ([0, 0], 1, 16, 8)]
+    for _ in range(10):
+        n = int(rng.integers(1, 3000))
+        cases.append((list(rng.integers(0, 9000, size=n)), int(rng.choice([1, 2])),
+                      int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 2000))))
+    for seqlens, s_q, h_q, parts in cases:
+        sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+        meta, sb, _ = mla.get_metadata(sl, s_q, h_q, parts)
+        torch.cuda.synchronize()
+        ref_meta, ref_sb = oracle.plan(seqlens, parts, oracle.plan_overhead(s_q, h_q))
+        np.testing.assert_array_equal(meta.cpu().numpy(), np.array(ref_meta, dtype=np.int32))
+        np.testing.assert_array_equal(sb.cpu().numpy(), np.array(ref_sb, dtype=np.int32))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    case = W.make_case([700, 1500, 90], 1, 64, seed=9)
+    dev = to_device(case)
+    o1, l1 = run_gpu(case, dev=dev)
+    o2, l2 = run_gpu(case, dev=dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_page_permutation_does_not_change_gpu_result():
+    a = W.make_case([300, 1000], 1, 16, seed=10, permute=False)
+    b = W.make_case([300, 1000], 1, 16, seed=10, permute=True, spare_pages=5)
+    oa, la = run_gpu(a, num_parts=8)
+    ob, lb = run_gpu(b, num_parts=8)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("name", ["membound", "computebound", "fp8", "longctx"])
+def test_full_size_workloads_on_sampled_rows(name):
+    case = W.make_config(name)
+    print(f"{name}: batch={case.batch} pages={case.num_pages}", flush=True)
+    out, lse = run_gpu(case)
+    rows = sample_rows(case, 40, seed=11)
+    ref_out, ref_lse, _ = oracle.decode_rows(case.q, case.cache, case.kind, case.block_table,
+                                             case.seqlens, case.scale, case.causal, rows)
+    b, i, h = rows[:, 0], rows[:, 1], rows[:, 2]
+    compare(out[b, i, h], lse[b, i, h], ref_out, ref_lse, name)
+    # a property over every row: all outputs finite
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))

@@ -183,3 +183,50 @@ def algorithmic_flops(seqlens, s_q, h_q, causal):
         n = L - (s_q - 1 - i) if causal else L
         total += int(np.clip(n, 0, None).sum())
     return 2 * h_q * (D_QK + D_V) * total
+
+
+def make_config_device(name, device="cuda"):
+    """The same workload shapes generated directly in device memory (torch's
+    seeded CUDA generator; N(0,1) rounded to bf16; shuffled physical pages).
+    For timing runs, where regenerating gigabytes on the host would dominate.
+    Returns (q, kcache, block_table, seqlens, s_q, h_q, causal, scale, fp8)."""
+    import torch
+
+    cfg = CONFIGS[name]
+    rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
+    seqlens = config_seqlens(name, rng)
+    s_q, h_q, fp8 = cfg["s_q"], cfg["h_q"], cfg["fp8"]
+    batch = seqlens.shape[0]
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg["seed"])
+    q = torch.randn((batch, s_q, h_q, D_QK), generator=g, device=device).to(torch.bfloat16)
+    pages = (seqlens.astype(np.int64) + PAGE - 1) // PAGE
+    n_pages = int(pages.sum())
+    perm = torch.randperm(n_pages, generator=g, device=device).to(torch.int32)
+    width = int(pages.max())
+    bt = torch.full((batch, width), -1, dtype=torch.int32, device=device)
+    starts = np.concatenate([[0], np.cumsum(pages)[:-1]])
+    for b in range(batch):
+        bt[b, : pages[b]] = perm[starts[b]: starts[b] + pages[b]]
+    if not fp8:
+        kc = torch.empty((n_pages, PAGE, D_QK), dtype=torch.bfloat16, device=device)
+        chunk = 1024
+        for p0 in range(0, n_pages, chunk):
+            p1 = min(n_pages, p0 + chunk)
+            kc[p0:p1] = torch.randn((p1 - p0, PAGE, D_QK), generator=g, device=device).to(torch.bfloat16)
+    else:
+        kc = torch.empty((n_pages, PAGE, FP8_RECORD), dtype=torch.uint8, device=device)
+        chunk = 1024
+        for p0 in range(0, n_pages, chunk):
+            p1 = min(n_pages, p0 + chunk)
+            x = torch.randn((p1 - p0, PAGE, D_QK), generator=g, device=device).to(torch.bfloat16).float()
+            lat = x[..., :D_V].reshape(p1 - p0, PAGE, D_V // FP8_TILE, FP8_TILE)
+            scale = lat.abs().amax(dim=-1) / E4M3_MAX
+            safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+            codes = (lat / safe[..., None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+            codes = torch.where(scale[..., None] > 0, codes.view(torch.uint8), 0)
+            kc[p0:p1, :, :D_V] = codes.reshape(p1 - p0, PAGE, D_V)
+            kc[p0:p1, :, D_V:D_V + 16] = scale.contiguous().view(torch.uint8).reshape(p1 - p0, PAGE, 16)
+            kc[p0:p1, :, D_V + 16:] = x[..., D_V:].to(torch.bfloat16).contiguous().view(torch.uint8)
+    sl = torch.from_numpy(seqlens).to(device)
+    return q, kc, bt, sl, s_q, h_q, cfg["causal"], 1.0 / math.sqrt(D_QK), fp8
