@@ -36,6 +36,8 @@ def parse():
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run plain 1 GiB device copies (to scale HBM counters)")
     return p.parse_args()
 
 
@@ -173,6 +175,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones((n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
     main_r = Runner(args.workload)
     m = main_r.measure(args.steps, args.warmup)
     rep = main_r.report(m)

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.hip", "plan.hip", "decode.hip", "combine.hip"]
+SOURCES = ["api.hip", "plan.hip", "decode.hip", "decode_rows64.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -16,15 +16,18 @@ FLAGS = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
-    # MFMA accumulators in VGPRs: the online-softmax rescale then multiplies
-    # them in place instead of shuttling them through AGPR copies
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the direct-to-LDS asm names m0 as clobbered; the compiler reserves m0
+    "-Wno-inline-asm",
 ]
+# Per-source extras.  decode.hip: MFMA accumulators in VGPRs, so the
+# online-softmax rescale multiplies them in place instead of shuttling them
+# through AGPR copies (its accumulators fit in the 256 VGPRs).
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

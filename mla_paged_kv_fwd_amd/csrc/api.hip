@@ -12,6 +12,7 @@ void plan_host(const int32_t *seqlens, int batch, int c, int num_parts, int32_t 
                int32_t *split_base);
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 int decode_rows_per_group();
+hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -21,6 +22,10 @@ static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::k
               "header and kernels disagree");
 
 namespace {
+
+// Kernel choice: 64 query rows per work-group with specialised score / value
+// waves when a request has at least 64 rows; 16 rows per work-group otherwise.
+bool use_rows64(int kv_format, int M) { return kv_format == 0 && M >= 64; }
 
 bool shape_supported(int s_q, int h_q) {
     return (s_q == 1 || s_q == 2) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
@@ -76,10 +81,16 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.h_q = h_q;
     a.M = M;
     a.num_parts = num_parts;
-    a.row_groups = M / mla::decode_rows_per_group();
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
-    hipError_t e = mla::launch_decode(a, kv_format == 1, (hipStream_t)stream);
+    hipError_t e;
+    if (use_rows64(kv_format, M)) {
+        a.row_groups = M / 64;
+        e = mla::launch_decode_rows64(a, (hipStream_t)stream);
+    } else {
+        a.row_groups = M / mla::decode_rows_per_group();
+        e = mla::launch_decode(a, kv_format == 1, (hipStream_t)stream);
+    }
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -138,8 +149,12 @@ int mla_default_num_parts(int device, int s_q, int h_q) {
             return MLA_ERR_HIP;
         g_cu_count[device] = cus;
     }
-    // one work-group of the row-group kernel per CU and part
+    // one work-group per CU: a part spans M / 64 work-groups in the 64-row
+    // kernel and M / 16 (run in several rounds) in the 16-row kernel
+    const int M = s_q * h_q;
     int parts = g_cu_count[device];
+    if (use_rows64(0, M)) parts = parts / (M / 64);
+    parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
 }
 

@@ -1,0 +1,387 @@
+// MLA decode attention for many query rows per request (s_q * h_q >= 64):
+// gfx950 kernel with specialised waves.
+//
+// A work-group (4 waves, one per SIMD) owns one split-KV part and one group of
+// 64 query rows.  It walks the part's pages in 32-token half-pages:
+//   - waves 0, 1 ("score waves") each hold 32 query rows of Q in registers and
+//     compute S^T (32 tokens x 32 rows) = K . Q^T on 32x32x16 bf16 MFMAs, then
+//     the online softmax of their rows, and hand P (bf16) plus the per-row
+//     rescale factor to the value waves through LDS;
+//   - waves 2, 3 ("value waves") each own 256 of the 512 output dims for all
+//     64 rows and accumulate O^T (dims x rows) += V^T . P^T, one half-page
+//     behind the score waves.
+// Half-pages stream HBM -> LDS with direct-to-LDS loads into a 4-deep ring:
+// during step t the score waves read half-page t, the value waves half-page
+// t-1, and half-pages t+1, t+2 are in flight.  One work-group barrier per step.
+//
+// Half-page LDS layout: 16-byte chunk c (of 72) of token t (of 32) sits in
+// slot c * 32 + (t ^ 8 * (c & 1)).  The XOR swizzle keeps both the K operand
+// reads (ds_read_b128) and the transposed V operand reads (ds_read_b64_tr_b16)
+// free of bank conflicts.
+#include <math.h>
+
+#include "common.h"
+#include "device_util.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsWG = 64;                       // query rows per work-group
+constexpr int kHalf = 32;                         // tokens per step
+constexpr int kHalfBytes = kHalf * kTokBytesBf16;  // 36864
+constexpr int kRing = 4;
+constexpr int kDmaPerWave = kHalfBytes / 1024 / 4;  // 9 direct-to-LDS loads per wave per step
+constexpr int kPOff = kRing * kHalfBytes;         // P hand-off: 2 x (2 row tiles x 2 k-steps x 1 KB)
+constexpr int kPBytes = 4096;
+constexpr int kFlagOff = kPOff + 2 * kPBytes;     // restart flags of the two score waves
+constexpr int kStatOff = kFlagOff + 64;           // final (m, l) per row
+constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
+constexpr float kGrowLog2 = 16.f;  // reference headroom before a segment restarts
+constexpr int kXStride = kDV + 4;                 // padded row stride of the output stage
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int slot_of(int c, int t) { return c * 32 + (t ^ (8 * (c & 1))); }
+
+// Direct-to-LDS loads of this wave's 9 of the 36 one-KB blocks of a half-page.
+// Block s holds chunks 2s, 2s+1 of all 32 tokens: lane l fetches chunk
+// 2s + l/32 of token (l % 32) ^ (8 * (l / 32)), which lands in slot 64 s + l.
+__device__ __forceinline__ void issue_half(const unsigned char *kv, int64_t phys, int tok0,
+                                           int tok_last, int w, int lane, unsigned dst) {
+    const int h = lane >> 5;
+    int t = tok0 + ((lane & 31) ^ (8 * h));
+    t = t < tok_last ? t : tok_last;
+    const unsigned char *src = kv + (phys * kPage + t) * kTokBytesBf16 + h * 16;
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        const int s = w * kDmaPerWave + k;
+        dma16(src + s * 32, __builtin_amdgcn_readfirstlane(dst + s * 1024));
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_own_dma(bool more) {
+    if (more) wait_vmcnt<N>(); else wait_vmcnt<0>();
+}
+
+// One request segment of a part: pages j0..j1 of request b.
+struct Segment {
+    int b, L, npages, j0, rank, nsplit, H;  // H = number of 32-token steps
+    const int32_t *bt;
+};
+
+// Calls f(seg) for every non-empty request segment of a part, in order.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int32_t *seqlens,
+                                                 const int32_t *split_base,
+                                                 const int32_t *block_table, int64_t bt_stride,
+                                                 F &&f) {
+    const int b_first = mrow[0], j_first = mrow[1], b_last = mrow[2], j_last = mrow[3];
+    for (int b = b_first; b <= b_last; ++b) {
+        Segment sg;
+        sg.b = b;
+        sg.L = seqlens[b];
+        if (sg.L <= 0) continue;
+        sg.npages = (sg.L + kPage - 1) / kPage;
+        sg.j0 = (b == b_first) ? j_first : 0;
+        const int j1 = (b == b_last) ? j_last : sg.npages - 1;
+        sg.rank = (b == b_first) ? mrow[4] : 0;
+        sg.nsplit = split_base[b + 1] - split_base[b];
+        sg.bt = block_table + (int64_t)b * bt_stride;
+        // the last page may hold a single half
+        const int tok_end = (j1 == sg.npages - 1) ? sg.L : (j1 + 1) * kPage;
+        sg.H = (tok_end - sg.j0 * kPage + kHalf - 1) / kHalf;
+        f(sg);
+    }
+}
+
+// Direct-to-LDS loads of half-page t of a segment (this wave's share).
+__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int w,
+                                           int lane, unsigned ring0) {
+    const int j = sg.j0 + (t >> 1);
+    const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
+    issue_half(kv, sg.bt[j], (t & 1) * kHalf, tok_last, w, lane, ring0 + (t % kRing) * kHalfBytes);
+}
+
+// All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
+// segment's split slot (fp32), four threads per row, coalesced.
+__device__ __forceinline__ void write_rows(const DecodeArgs &a, const Segment &sg,
+                                           const int32_t *split_base, const float *X,
+                                           const float *row_sum, int row0, int tid) {
+    const int r = tid >> 2, c0 = (tid & 3) * 128;
+    const int orow = row0 + r;
+    const float *xr = X + r * kXStride + c0;
+    const float lsum = row_sum[r];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (sg.nsplit == 1) {
+        uint16_t *dst = a.out + ((int64_t)sg.b * a.M + orow) * kDV + c0;
+#pragma unroll 4
+        for (int d = 0; d < 128; d += 8) {
+            const f32x4 u0 = *(const f32x4 *)(xr + d) * inv, u1 = *(const f32x4 *)(xr + d + 4) * inv;
+            u32x4 pk;
+            pk[0] = (unsigned)f32_to_bf16_bits(u0[0]) | ((unsigned)f32_to_bf16_bits(u0[1]) << 16);
+            pk[1] = (unsigned)f32_to_bf16_bits(u0[2]) | ((unsigned)f32_to_bf16_bits(u0[3]) << 16);
+            pk[2] = (unsigned)f32_to_bf16_bits(u1[0]) | ((unsigned)f32_to_bf16_bits(u1[1]) << 16);
+            pk[3] = (unsigned)f32_to_bf16_bits(u1[2]) | ((unsigned)f32_to_bf16_bits(u1[3]) << 16);
+            *(u32x4 *)(dst + d) = pk;
+        }
+    } else {
+        float *dst = a.o_part + ((int64_t)(split_base[sg.b] + sg.rank) * a.M + orow) * kDV + c0;
+#pragma unroll 4
+        for (int d = 0; d < 128; d += 4) *(f32x4 *)(dst + d) = *(const f32x4 *)(xr + d) * inv;
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
+    const DecodeArgs a, const uint16_t *__restrict__ q, const unsigned char *__restrict__ kv,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seqlens,
+    const int32_t *__restrict__ meta, const int32_t *__restrict__ split_base) {
+    // The read-only tables arrive as separate restrict-qualified arguments so
+    // that their uniform reads compile to scalar loads.
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kLdsBytes];
+    lds_u8 *smem = (lds_u8 *)smem_raw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: the role branches below hold barriers and must be
+    // compiled as uniform branches
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // blockIdx -> (part, row group), row groups of a part on one XCD
+    const int lin = blockIdx.x;
+    const int rest = lin >> 3;
+    const int rg = rest % a.row_groups;
+    const int part = (rest / a.row_groups) * 8 + (lin & 7);
+    if (part >= a.num_parts) return;
+    const int32_t *mrow = meta + part * kMetaInts;
+    if (mrow[0] < 0) return;
+
+    const unsigned ring0 = lds_addr(smem);
+    volatile __attribute__((address_space(3))) int *flag_lds =
+        (volatile __attribute__((address_space(3))) int *)(smem + kFlagOff);
+    float *stat_lds = (float *)(smem_raw + kStatOff);
+    float *X = (float *)smem_raw;  // output stage [64][kXStride], over the ring
+    const int row0 = rg * kRowsWG;
+
+    if (w < 2) {
+        // ================= score waves: rows row0 + 32 w + (lane % 32)
+        const int row = row0 + 32 * w + l32;
+        const int qi = row / a.h_q;
+        const int koff = (lane ^ (8 * h)) * 16;  // this lane's slot within a 1 KB block
+        for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            issue_step(sg, kv, 0, w, lane, ring0);
+            if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+            int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
+            n_visible = n_visible > 0 ? n_visible : 0;
+            // Q^T operand for 32x32x16: lane holds dims 16 ks + 8 h .. +8 of its row
+            bf16x8 qf[kDQk / 16];
+            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row) * kDQk + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < kDQk / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+#pragma unroll
+            for (int ks = 0; ks < kDQk / 16; ++ks) asm volatile("" : : "v"(qf[ks]));
+            // Exponent reference per row.  It is fixed for a pass over the
+            // segment, so the value waves never rescale their accumulators: a
+            // row whose running max exceeds it by more than kGrowLog2 makes the
+            // whole work-group restart the segment with the larger reference
+            // (rows that have not seen a key yet adopt their first max freely,
+            // their accumulators being zero).
+            float m_seen = -INFINITY, m, lsum;
+            bool again;
+            do {  // one pass over the segment; repeated only after a restart
+                m = m_seen;
+                lsum = 0.f;
+                again = false;
+                if (lane == 0) flag_lds[w] = 0;
+                for (int t = 0; t <= sg.H; ++t) {
+                    wait_own_dma<kDmaPerWave>(t + 1 < sg.H);
+                    __syncthreads();
+                    if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {  // restart with the larger reference
+                        again = true;
+                        break;
+                    }
+                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, w, lane, ring0);
+                    if (t == sg.H) break;
+                    const lds_u8 *S = smem + (t % kRing) * kHalfBytes;
+                    f32x16 sa = {}, sb = {};
+                    constexpr int kPre = 8;  // K fragments in flight ahead of the MFMAs
+                    bf16x8 kf[kPre];
+    #pragma unroll
+                    for (int ks = 0; ks < kPre; ++ks)
+                        kf[ks] = *(const bf16x8 __attribute__((address_space(3))) *)(S + ks * 1024 + koff);
+    #pragma unroll
+                    for (int ks = 0; ks < kDQk / 16; ++ks) {
+                        const bf16x8 cur = kf[ks % kPre];
+                        if (ks + kPre < kDQk / 16)
+                            kf[ks % kPre] = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks + kPre) * 1024 + koff);
+                        if (ks & 1)
+                            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sb, 0, 0, 0);
+                        else
+                            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sa, 0, 0, 0);
+                    }
+                    // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row
+                    const int tok_base = sg.j0 * kPage + t * kHalf + 4 * h;
+                    float x[16], mloc = -INFINITY;
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int tok = tok_base + 8 * (i >> 2) + (i & 3);
+                        x[i] = (tok < n_visible) ? (sa[i] + sb[i]) * a.scale_log2 : -INFINITY;
+                        mloc = fmaxf(mloc, x[i]);
+                    }
+                    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                    m_seen = fmaxf(m_seen, mloc);
+                    if (m == -INFINITY) m = mloc;  // first keys of this row
+                    const bool overflow = mloc > m + kGrowLog2;
+                    if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) flag_lds[w] = 1;
+                    const float m_ref = (m == -INFINITY) ? 0.f : m;
+                    float psum = 0.f;
+                    unsigned pk[8];
+    #pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(x[i] - m_ref);
+                        const float p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_ref);
+                        psum += p0 + p1;
+                        pk[i >> 1] = (unsigned)f32_to_bf16_bits(p0) | ((unsigned)f32_to_bf16_bits(p1) << 16);
+                    }
+                    lsum += psum;
+                    // P^T operand blocks: (row tile w, k-step kk) -> 1 KB at P + (2 w + kk) KB
+                    lds_u8 *P = smem + kPOff + (t & 1) * kPBytes;
+                    *(u32x4 __attribute__((address_space(3))) *)(P + (2 * w + 0) * 1024 + lane * 16) =
+                        (u32x4){pk[0], pk[1], pk[2], pk[3]};
+                    *(u32x4 __attribute__((address_space(3))) *)(P + (2 * w + 1) * 1024 + lane * 16) =
+                        (u32x4){pk[4], pk[5], pk[6], pk[7]};
+
+                }
+                if (again) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    issue_step(sg, kv, 0, w, lane, ring0);
+                    if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+                }
+            } while (again);
+            lsum += __shfl_xor(lsum, 32);
+            if (h == 0) {
+                stat_lds[kRowsWG + 32 * w + l32] = lsum;
+                const float lse_val =
+                    lsum > 0.f ? (m + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+                if (sg.nsplit == 1)
+                    a.lse[(int64_t)sg.b * a.M + row] = lse_val;
+                else
+                    a.lse_part[(int64_t)(split_base[sg.b] + sg.rank) * a.M + row] = lse_val;
+            }
+            __syncthreads();  // stats visible to the value waves
+            __syncthreads();  // value waves have staged the output
+            write_rows(a, sg, split_base, X, stat_lds + kRowsWG, row0, tid);
+            __syncthreads();  // LDS free for the next segment
+        });
+    } else {
+        // ================= value waves: dims d0 .. d0 + 255 for all 64 rows
+        const int d0 = (w - 2) * 256;
+        // transposed V reads: group g = lane / 16 covers dims 16 (g & 1) + (lane % 16)
+        // and tokens 4 (g >> 1) + r (first read) / 8 + 4 (g >> 1) + r (second read)
+        const int g = lane >> 4, i16 = lane & 15;
+        const int cv = (d0 >> 3) + 2 * (g & 1) + ((i16 & 3) >> 1);  // chunk for k-step 0 reads
+        const int tv = 4 * (g >> 1) + (i16 >> 2);
+        const int vb0 = slot_of(cv, tv) * 16 + 8 * (i16 & 1);
+        const int vb1 = slot_of(cv, tv + 8) * 16 + 8 * (i16 & 1);
+        for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            issue_step(sg, kv, 0, w, lane, ring0);
+            if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+            f32x16 o[2][8];
+            bool again;
+            do {  // one pass over the segment; repeated only after a restart
+                // Zero the accumulators with MFMAs (0 x 0 + 0) so they are born
+                // in the accumulator registers; plain zero stores get hoisted
+                // into 256 VGPRs of constants by the compiler.
+                u32x4 zw;
+                asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                             : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
+                const bf16x8 zf = __builtin_bit_cast(bf16x8, zw);
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt)
+                        o[r][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, (f32x16){}, 0, 0, 0);
+                again = false;
+                for (int t = 0; t <= sg.H; ++t) {
+                    wait_own_dma<kDmaPerWave>(t + 1 < sg.H);
+                    __syncthreads();
+                    if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {  // the score waves restart the segment
+                        again = true;
+                        break;
+                    }
+                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, w, lane, ring0);
+                    if (t == 0) continue;
+                    const int tp = t - 1;  // half-page processed this step
+                    const lds_u8 *V = smem + (tp % kRing) * kHalfBytes;
+                    const lds_u8 *P = smem + kPOff + (tp & 1) * kPBytes;
+    #pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const bf16x8 p0 = *(const bf16x8 __attribute__((address_space(3))) *)(P + (0 + kk) * 1024 + lane * 16);
+                        const bf16x8 p1 = *(const bf16x8 __attribute__((address_space(3))) *)(P + (2 + kk) * 1024 + lane * 16);
+                        bf16x8 vf[8];
+    #pragma unroll
+                        for (int dt = 0; dt < 8; ++dt) {
+                            // chunk advances by 4 per 32 dims, token by 16 per k-step; the
+                            // swizzle term depends only on chunk parity, which is unchanged
+                            const int off = dt * 4 * 32 * 16 + kk * 16 * 16;
+                            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (i16x4 __attribute__((address_space(3))) *)(V + vb0 + off));
+                            const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (i16x4 __attribute__((address_space(3))) *)(V + vb1 + off));
+                            const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+                            vf[dt] = __builtin_bit_cast(bf16x8, v8);
+                        }
+    #pragma unroll
+                        for (int dt = 0; dt < 8; ++dt) {
+                            o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p0, o[0][dt], 0, 0, 0);
+                            o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p1, o[1][dt], 0, 0, 0);
+                        }
+                    }
+
+                }
+                if (again) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    issue_step(sg, kv, 0, w, lane, ring0);
+                    if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+                }
+            } while (again);
+            __syncthreads();  // score waves' final stats visible
+            // Stage O^T (unnormalised fp32) in LDS as [row][dim]; the ring is free.
+            // Plain stores straight from the accumulators (no arithmetic), so
+            // no accumulator tile has to pass through VGPRs.
+            // lane holds, for row tile r, row 32 r + lane % 32 and dims
+            // d0 + 32 dt + 8 (i / 4) + 4 h + (i % 4)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                float *xrow = X + (32 * r + l32) * kXStride + d0 + 4 * h;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const f32x16 &v = o[r][dt];
+                        *(f32x4 *)(xrow + 32 * dt + 8 * qd) =
+                            (f32x4){v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]};
+                    }
+            }
+            __syncthreads();  // staged output complete
+            write_rows(a, sg, split_base, X, stat_lds + kRowsWG, row0, tid);
+            __syncthreads();  // LDS free for the next segment
+        });
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream) {
+    const int groups8 = (a.num_parts + 7) / 8;
+    const dim3 grid(groups8 * 8 * a.row_groups), block(kThreads);
+    hipLaunchKernelGGL(decode_rows64_kernel, grid, block, 0, stream, a, a.q, a.kv, a.block_table,
+                       a.seqlens, a.meta, a.split_base);
+    return hipGetLastError();
+}
+
+}  // namespace mla
