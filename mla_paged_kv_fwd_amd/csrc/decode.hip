@@ -15,10 +15,11 @@
 // its P^T operand, and every lane's softmax statistics belong to one query
 // row (lane % 16).
 //
-// LDS slice layout ("chunk-major"): 16-byte chunk c of token t of a slice sits
-// at byte (c * 16 + t) * 16.  With it the K operand of QK^T is one contiguous
-// 1 KB ds_read_b128 per wave, and the V^T operand of PV is a conflict-free
-// ds_read_b64_tr_b16 (4 tokens x 16 dims transposed per 16-lane group).
+// LDS slice layout ("chunk-major", swizzled): 16-byte chunk c of token t of a
+// slice sits in slot c * 16 + (t ^ 4 * (c & 1)).  The K operand of QK^T is
+// then one 1 KB ds_read_b128 block per wave, and the V^T operand of PV a
+// ds_read_b64_tr_b16 (4 tokens x 16 dims transposed per 16-lane group); the
+// XOR keeps both free of bank conflicts.
 #include <math.h>
 
 #include "common.h"
@@ -46,14 +47,18 @@ template <bool FP8>
 __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phys, int tok_last,
                                             int w, int lane, unsigned lds_dst) {
     const int lr = lane & 15, lg = lane >> 4;
-    int t = kSlice * w + lr;
-    t = t < tok_last ? t : tok_last;
     if constexpr (!FP8) {
+        // block s = chunks 4 s + lg of the slice's tokens; the swizzle puts
+        // token lr ^ 4 (lg & 1) in this lane's slot
+        int t = kSlice * w + (lr ^ (4 * (lg & 1)));
+        t = t < tok_last ? t : tok_last;
         const unsigned char *src = kv + (phys * kPage + t) * kTokBytesBf16 + lg * 16;
 #pragma unroll
         for (int s = 0; s < kLoadsBf16; ++s)
             dma16(src + s * 64, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
     } else {
+        int t = kSlice * w + lr;  // FP8 slices are not swizzled
+        t = t < tok_last ? t : tok_last;
         const unsigned char *rec = kv + (phys * kPage + t) * kTokBytesFp8;
 #pragma unroll
         for (int s = 0; s < kLoadsFp8; ++s) {
@@ -63,6 +68,9 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
         }
     }
 }
+
+// slot of chunk c of token t in a swizzled bf16 slice
+__device__ __forceinline__ int slot16(int c, int t) { return c * 16 + (t ^ (4 * (c & 1))); }
 
 // FP8 slice (chunk-major, 41 chunks x 16 tokens) -> bf16 slice (72 x 16).
 // The latent codes are converted exactly (every E4M3FN value is a bf16
@@ -84,16 +92,16 @@ __device__ __forceinline__ void dequant_slice(const lds_u8 *f8, lds_u8 *bf, int 
             packed[2 * q] = (unsigned)f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
             packed[2 * q + 1] = (unsigned)f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
         }
-        *(u32x4 __attribute__((address_space(3))) *)(bf + ((2 * c) * 16 + lr) * 16) =
+        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(2 * c, lr) * 16) =
             (u32x4){packed[0], packed[1], packed[2], packed[3]};
-        *(u32x4 __attribute__((address_space(3))) *)(bf + ((2 * c + 1) * 16 + lr) * 16) =
+        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(2 * c + 1, lr) * 16) =
             (u32x4){packed[4], packed[5], packed[6], packed[7]};
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int r = 33 + lg + 4 * k;  // RoPE chunk in the record
         const u32x4 v = *(const u32x4 __attribute__((address_space(3))) *)(f8 + (r * 16 + lr) * 16);
-        *(u32x4 __attribute__((address_space(3))) *)(bf + ((64 + r - 33) * 16 + lr) * 16) = v;
+        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(64 + r - 33, lr) * 16) = v;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -116,6 +124,7 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
                                              int lane, int tok0, int n_visible, float scale_log2,
                                              const f32x4 *tsc) {
     const int lr = lane & 15, lg = lane >> 4;
+    const int kl = lane ^ (4 * (lg & 1));  // slot of (chunk 4 ks + lg, token lr) in block ks
     // S^T (16 tokens x 16 rows) = K (16 x 576) . Q^T (576 x 16).  bf16 cache:
     // two accumulation chains.  FP8 cache: one chain per 128-dim scale tile
     // plus one for the RoPE dims, combined with the token scales afterwards.
@@ -124,8 +133,8 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kDQk / 32; ks += 2) {
-            const bf16x8 k0 = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks * 64 + lane) * 16);
-            const bf16x8 k1 = *(const bf16x8 __attribute__((address_space(3))) *)(S + ((ks + 1) * 64 + lane) * 16);
+            const bf16x8 k0 = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks * 64 + kl) * 16);
+            const bf16x8 k1 = *(const bf16x8 __attribute__((address_space(3))) *)(S + ((ks + 1) * 64 + kl) * 16);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks + 1], s1, 0, 0, 0);
         }
@@ -137,7 +146,7 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
         for (int t = 0; t < 5; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kDQk / 32; ++ks) {
-            const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks * 64 + lane) * 16);
+            const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks * 64 + kl) * 16);
             const int t = ks < 16 ? ks / 4 : 4;
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc[t], 0, 0, 0);
         }
@@ -188,7 +197,8 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
             pf[t][i] = (short)f32_to_bf16_bits(FP8 ? p[i] * tsc[i][t] : p[i]);
     }
     // O^T (512 dims x 16 rows) += V^T (512 x 16 tokens) . P^T (16 tokens x 16 rows)
-    const lds_u8 *vt = S + ((((lr & 3) >> 1) * 16 + 4 * lg + (lr >> 2)) * 16) + 8 * (lr & 1);
+    const int vp = (lr >> 1) & 1;  // chunk parity of this lane's V reads
+    const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ vp) + (lr >> 2)) * 16 + 8 * (lr & 1);
 #pragma unroll
     for (int dt = 0; dt < kDV / 16; ++dt) {
         const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

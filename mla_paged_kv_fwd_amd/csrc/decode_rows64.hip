@@ -15,9 +15,9 @@
 // t-1, and half-pages t+1, t+2 are in flight.  One work-group barrier per step.
 //
 // Half-page LDS layout: 16-byte chunk c (of 72) of token t (of 32) sits in
-// slot c * 32 + (t ^ 8 * (c & 1)).  The XOR swizzle keeps both the K operand
-// reads (ds_read_b128) and the transposed V operand reads (ds_read_b64_tr_b16)
-// free of bank conflicts.
+// slot c * 32 + (t ^ 4 * (c & 1)).  The XOR swizzle keeps both the K operand
+// reads (ds_read_b128, 8 lanes per LDS cycle) and the transposed V operand
+// reads (ds_read_b64_tr_b16, 16 lanes per cycle) free of bank conflicts.
 #include <math.h>
 
 #include "common.h"
@@ -44,15 +44,15 @@ constexpr int kXStride = kDV + 4;                 // padded row stride of the ou
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int slot_of(int c, int t) { return c * 32 + (t ^ (8 * (c & 1))); }
+__device__ __forceinline__ int slot_of(int c, int t) { return c * 32 + (t ^ (4 * (c & 1))); }
 
 // Direct-to-LDS loads of this wave's 9 of the 36 one-KB blocks of a half-page.
 // Block s holds chunks 2s, 2s+1 of all 32 tokens: lane l fetches chunk
-// 2s + l/32 of token (l % 32) ^ (8 * (l / 32)), which lands in slot 64 s + l.
+// 2s + l/32 of token (l % 32) ^ (4 * (l / 32)), which lands in slot 64 s + l.
 __device__ __forceinline__ void issue_half(const unsigned char *kv, int64_t phys, int tok0,
                                            int tok_last, int w, int lane, unsigned dst) {
     const int h = lane >> 5;
-    int t = tok0 + ((lane & 31) ^ (8 * h));
+    int t = tok0 + ((lane & 31) ^ (4 * h));
     t = t < tok_last ? t : tok_last;
     const unsigned char *src = kv + (phys * kPage + t) * kTokBytesBf16 + h * 16;
 #pragma unroll
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         // ================= score waves: rows row0 + 32 w + (lane % 32)
         const int row = row0 + 32 * w + l32;
         const int qi = row / a.h_q;
-        const int koff = (lane ^ (8 * h)) * 16;  // this lane's slot within a 1 KB block
+        const int koff = (lane ^ (4 * h)) * 16;  // this lane's slot within a 1 KB block
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
             issue_step(sg, kv, 0, w, lane, ring0);
             if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
@@ -221,6 +221,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         else
                             sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sa, 0, 0, 0);
                     }
+                    // keep kPre K reads in flight: kPre reads, then one MFMA per read
+                    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+                    for (int ks = 0; ks < kDQk / 16 - kPre; ++ks) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
                     // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row
                     const int tok_base = sg.j0 * kPage + t * kHalf + 4 * h;
                     float x[16], mloc = -INFINITY;
@@ -340,6 +348,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                             o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p1, o[1][dt], 0, 0, 0);
                         }
                     }
+                    // overlap reads and MFMAs: the first k-step's P and V reads,
+                    // then two MFMAs per two reads, then the remaining MFMAs
+                    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+                    for (int k = 0; k < 13; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 
                 }
                 if (again) {
