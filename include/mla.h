@@ -124,7 +124,7 @@ mla_status mla_get_metadata_host(const int32_t *seqlens_host, int batch, int s_q
  *   kcache      bf16 [num_pages][64][576]
  *   block_table int32 [batch][block_table_stride]
  *   seqlens     int32 [batch]
- *   softmax_scale  multiplies the full 576-dim dot product
+ *   softmax_scale  multiplies the full 576-dim dot product; finite and > 0
  *   causal      0 or 1 (only matters for s_q > 1)
  *   meta, split_base, num_parts   a plan from mla_get_metadata for the same
  *               seqlens, s_q, h_q

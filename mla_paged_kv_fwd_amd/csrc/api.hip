@@ -55,7 +55,7 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     if (kv_format != 0 && kv_format != 1) return MLA_ERR_INVALID_ARG;
     if (num_pages <= 0 || block_table_stride < 1) return MLA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
-    if (!isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
     mla_status st = check_plan_args(batch, s_q, h_q, num_parts);
     if (st != MLA_OK) return st;
     if (!workspace) return MLA_ERR_WORKSPACE;

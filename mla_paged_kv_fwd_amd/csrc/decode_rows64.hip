@@ -5,19 +5,25 @@
 // 64 query rows.  It walks the part's pages in 32-token half-pages:
 //   - waves 0, 1 ("score waves") each hold 32 query rows of Q in registers and
 //     compute S^T (32 tokens x 32 rows) = K . Q^T on 32x32x16 bf16 MFMAs, then
-//     the online softmax of their rows, and hand P (bf16) plus the per-row
-//     rescale factor to the value waves through LDS;
+//     the online softmax of their rows, and hand P (bf16) to the value waves
+//     through LDS;
 //   - waves 2, 3 ("value waves") each own 256 of the 512 output dims for all
 //     64 rows and accumulate O^T (dims x rows) += V^T . P^T, one half-page
-//     behind the score waves.
+//     behind the score waves.  They also issue every direct-to-LDS load, so
+//     the score waves never stall on the memory pipeline.
 // Half-pages stream HBM -> LDS with direct-to-LDS loads into a 4-deep ring:
 // during step t the score waves read half-page t, the value waves half-page
 // t-1, and half-pages t+1, t+2 are in flight.  One work-group barrier per step.
 //
-// Half-page LDS layout: 16-byte chunk c (of 72) of token t (of 32) sits in
-// slot c * 32 + (t ^ 4 * (c & 1)).  The XOR swizzle keeps both the K operand
-// reads (ds_read_b128, 8 lanes per LDS cycle) and the transposed V operand
-// reads (ds_read_b64_tr_b16, 16 lanes per cycle) free of bank conflicts.
+// Half-page LDS layout (36 KB, 2304 slots of 16 bytes).  Token tau (0..31),
+// 16-byte chunk c (0..71) of its 1152-byte row sits in slot
+//   64 * (9 * (tau / 8) + c / 8) + 8 * (tau % 8) + ((c % 8) ^ swz(tau)),
+//   swz(tau) = 4 * bit1(tau) + 2 * bit2(tau) + bit3(tau).
+// Each 1 KB block holds one 128-byte line of eight consecutive tokens, so a
+// direct-to-LDS load reads eight whole cache lines; the XOR keeps the K
+// operand reads (ds_read_b128, 16 lanes per LDS cycle) and the transposed V
+// operand reads (ds_read_b64_tr_b16, 16 or 32 lanes per cycle) free of bank
+// conflicts.
 #include <math.h>
 
 #include "common.h"
@@ -32,34 +38,50 @@ constexpr int kRowsWG = 64;                       // query rows per work-group
 constexpr int kHalf = 32;                         // tokens per step
 constexpr int kHalfBytes = kHalf * kTokBytesBf16;  // 36864
 constexpr int kRing = 4;
-constexpr int kDmaPerWave = kHalfBytes / 1024 / 4;  // 9 direct-to-LDS loads per wave per step
+constexpr int kDmaPerWave = kHalfBytes / 1024 / 2;  // 18 direct-to-LDS loads per value wave per step
 constexpr int kPOff = kRing * kHalfBytes;         // P hand-off: 2 x (2 row tiles x 2 k-steps x 1 KB)
 constexpr int kPBytes = 4096;
 constexpr int kFlagOff = kPOff + 2 * kPBytes;     // restart flags of the two score waves
 constexpr int kStatOff = kFlagOff + 64;           // final (m, l) per row
 constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
-constexpr float kGrowLog2 = 16.f;  // reference headroom before a segment restarts
+constexpr float kGrowLog2 = 16.f;  // reference headroom (log2 units) before a segment restarts
 constexpr int kXStride = kDV + 4;                 // padded row stride of the output stage
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int slot_of(int c, int t) { return c * 32 + (t ^ (4 * (c & 1))); }
+// XOR term of the half-page layout for token tau (bits 1, 2, 3 of tau).
+__device__ __forceinline__ int swz(int tau) {
+    return 4 * ((tau >> 1) & 1) + 2 * ((tau >> 2) & 1) + ((tau >> 3) & 1);
+}
 
-// Direct-to-LDS loads of this wave's 9 of the 36 one-KB blocks of a half-page.
-// Block s holds chunks 2s, 2s+1 of all 32 tokens: lane l fetches chunk
-// 2s + l/32 of token (l % 32) ^ (4 * (l / 32)), which lands in slot 64 s + l.
+// Direct-to-LDS loads of value wave v's 18 of the 36 one-KB blocks of a
+// half-page: token groups 2v, 2v+1 (8 tokens each), line 0..8 of each row.
+// Lane l covers token 8 G + l / 8 and, within the 128-byte line, the chunk
+// whose swizzled slot is l % 8.  Tokens past tok_last re-read tok_last.
 __device__ __forceinline__ void issue_half(const unsigned char *kv, int64_t phys, int tok0,
-                                           int tok_last, int w, int lane, unsigned dst) {
-    const int h = lane >> 5;
-    int t = tok0 + ((lane & 31) ^ (4 * h));
-    t = t < tok_last ? t : tok_last;
-    const unsigned char *src = kv + (phys * kPage + t) * kTokBytesBf16 + h * 16;
+                                           int tok_last, int v, int lane, unsigned dst) {
+    const int a = lane >> 3, b = lane & 7;
 #pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {
-        const int s = w * kDmaPerWave + k;
-        dma16(src + s * 32, __builtin_amdgcn_readfirstlane(dst + s * 1024));
+    for (int g2 = 0; g2 < 2; ++g2) {
+        const int G = 2 * v + g2;
+        const int tau = 8 * G + a;
+        int t = tok0 + tau;
+        t = t < tok_last ? t : tok_last;
+        const unsigned char *src =
+            kv + (phys * kPage + t) * kTokBytesBf16 + 16 * (b ^ swz(tau));
+#pragma unroll
+        for (int lam = 0; lam < 9; ++lam)
+            dma16(src + 128 * lam, __builtin_amdgcn_readfirstlane(dst + (9 * G + lam) * 1024));
     }
+}
+
+// Both halves' maximum for lanes l and l ^ 32.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int N>
@@ -98,12 +120,12 @@ __device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int3
     }
 }
 
-// Direct-to-LDS loads of half-page t of a segment (this wave's share).
-__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int w,
+// Direct-to-LDS loads of half-page t of a segment (value wave v's share).
+__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
                                            int lane, unsigned ring0) {
     const int j = sg.j0 + (t >> 1);
     const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
-    issue_half(kv, sg.bt[j], (t & 1) * kHalf, tok_last, w, lane, ring0 + (t % kRing) * kHalfBytes);
+    issue_half(kv, sg.bt[j], (t & 1) * kHalf, tok_last, v, lane, ring0 + (t % kRing) * kHalfBytes);
 }
 
 // All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
@@ -169,12 +191,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         // ================= score waves: rows row0 + 32 w + (lane % 32)
         const int row = row0 + 32 * w + l32;
         const int qi = row / a.h_q;
-        const int koff = (lane ^ (4 * h)) * 16;  // this lane's slot within a 1 KB block
+        const float c = a.scale_log2;  // > 0
+        const float grow = kGrowLog2 / c;
+        // K operand of k-step ks for this lane: token lane % 32, chunk 2 ks + h,
+        // at kofs[ks % 4] + 1024 (ks / 4) in the half-page
+        int kofs[4];
+        {
+            const int tau = l32, y = h ^ swz(tau);
+#pragma unroll
+            for (int k3 = 0; k3 < 4; ++k3)
+                kofs[k3] = 9216 * (tau >> 3) + 128 * (tau & 7) + 16 * ((2 * k3) ^ y);
+        }
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
-            issue_step(sg, kv, 0, w, lane, ring0);
-            if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
             int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
             n_visible = n_visible > 0 ? n_visible : 0;
+            const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;  // every row sees these
             // Q^T operand for 32x32x16: lane holds dims 16 ks + 8 h .. +8 of its row
             bf16x8 qf[kDQk / 16];
             const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row) * kDQk + 8 * h;
@@ -182,12 +213,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
             for (int ks = 0; ks < kDQk / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 #pragma unroll
             for (int ks = 0; ks < kDQk / 16; ++ks) asm volatile("" : : "v"(qf[ks]));
-            // Exponent reference per row.  It is fixed for a pass over the
-            // segment, so the value waves never rescale their accumulators: a
-            // row whose running max exceeds it by more than kGrowLog2 makes the
-            // whole work-group restart the segment with the larger reference
-            // (rows that have not seen a key yet adopt their first max freely,
-            // their accumulators being zero).
+            // Exponent reference per row (raw score units).  It is fixed for a
+            // pass over the segment, so the value waves never rescale their
+            // accumulators: a row whose running max exceeds it by more than
+            // kGrowLog2 (after scaling) makes the whole work-group restart the
+            // segment with the larger reference (rows that have not seen a key
+            // yet adopt their first max freely, their accumulators being zero).
             float m_seen = -INFINITY, m, lsum;
             bool again;
             do {  // one pass over the segment; repeated only after a restart
@@ -196,30 +227,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 again = false;
                 if (lane == 0) flag_lds[w] = 0;
                 for (int t = 0; t <= sg.H; ++t) {
-                    wait_own_dma<kDmaPerWave>(t + 1 < sg.H);
                     __syncthreads();
                     if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {  // restart with the larger reference
                         again = true;
                         break;
                     }
-                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, w, lane, ring0);
                     if (t == sg.H) break;
                     const lds_u8 *S = smem + (t % kRing) * kHalfBytes;
-                    f32x16 sa = {}, sb = {};
+                    f32x16 sacc = {};
                     constexpr int kPre = 8;  // K fragments in flight ahead of the MFMAs
                     bf16x8 kf[kPre];
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < kPre; ++ks)
-                        kf[ks] = *(const bf16x8 __attribute__((address_space(3))) *)(S + ks * 1024 + koff);
-    #pragma unroll
+                        kf[ks] = *(const bf16x8 __attribute__((address_space(3))) *)(S + kofs[ks & 3] + 1024 * (ks >> 2));
+#pragma unroll
                     for (int ks = 0; ks < kDQk / 16; ++ks) {
                         const bf16x8 cur = kf[ks % kPre];
-                        if (ks + kPre < kDQk / 16)
-                            kf[ks % kPre] = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks + kPre) * 1024 + koff);
-                        if (ks & 1)
-                            sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sb, 0, 0, 0);
-                        else
-                            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sa, 0, 0, 0);
+                        const int kn = ks + kPre;
+                        if (kn < kDQk / 16)
+                            kf[ks % kPre] = *(const bf16x8 __attribute__((address_space(3))) *)(S + kofs[kn & 3] + 1024 * (kn >> 2));
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc, 0, 0, 0);
                     }
                     // keep kPre K reads in flight: kPre reads, then one MFMA per read
                     __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
@@ -230,28 +257,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
                     // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row
-                    const int tok_base = sg.j0 * kPage + t * kHalf + 4 * h;
-                    float x[16], mloc = -INFINITY;
-    #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int tok = tok_base + 8 * (i >> 2) + (i & 3);
-                        x[i] = (tok < n_visible) ? (sa[i] + sb[i]) * a.scale_log2 : -INFINITY;
-                        mloc = fmaxf(mloc, x[i]);
+                    const int tok0 = sg.j0 * kPage + t * kHalf;
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[i] = sacc[i];
+                    if (tok0 + kHalf > n_visible_all) {  // the causal edge or the segment's end
+                        const int tok_base = tok0 + 4 * h;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            x[i] = (tok_base + 8 * (i >> 2) + (i & 3) < n_visible) ? x[i] : -INFINITY;
                     }
-                    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                    float mloc = x[0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+                    mloc = max_xor32(mloc);
                     m_seen = fmaxf(m_seen, mloc);
                     if (m == -INFINITY) m = mloc;  // first keys of this row
-                    const bool overflow = mloc > m + kGrowLog2;
+                    const bool overflow = mloc > m + grow;
                     if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) flag_lds[w] = 1;
-                    const float m_ref = (m == -INFINITY) ? 0.f : m;
+                    const float mc = (m == -INFINITY) ? 0.f : m * c;
                     float psum = 0.f;
                     unsigned pk[8];
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 16; i += 2) {
-                        const float p0 = __builtin_amdgcn_exp2f(x[i] - m_ref);
-                        const float p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_ref);
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -mc));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i + 1], c, -mc));
                         psum += p0 + p1;
-                        pk[i >> 1] = (unsigned)f32_to_bf16_bits(p0) | ((unsigned)f32_to_bf16_bits(p1) << 16);
+                        pk[i >> 1] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
                     }
                     lsum += psum;
                     // P^T operand blocks: (row tile w, k-step kk) -> 1 KB at P + (2 w + kk) KB
@@ -260,20 +292,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         (u32x4){pk[0], pk[1], pk[2], pk[3]};
                     *(u32x4 __attribute__((address_space(3))) *)(P + (2 * w + 1) * 1024 + lane * 16) =
                         (u32x4){pk[4], pk[5], pk[6], pk[7]};
-
                 }
                 if (again) {
                     wait_vmcnt<0>();
                     __syncthreads();
-                    issue_step(sg, kv, 0, w, lane, ring0);
-                    if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
                 }
             } while (again);
             lsum += __shfl_xor(lsum, 32);
             if (h == 0) {
                 stat_lds[kRowsWG + 32 * w + l32] = lsum;
                 const float lse_val =
-                    lsum > 0.f ? (m + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+                    lsum > 0.f ? (m * c + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
                 if (sg.nsplit == 1)
                     a.lse[(int64_t)sg.b * a.M + row] = lse_val;
                 else
@@ -286,17 +315,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         });
     } else {
         // ================= value waves: dims d0 .. d0 + 255 for all 64 rows
-        const int d0 = (w - 2) * 256;
-        // transposed V reads: group g = lane / 16 covers dims 16 (g & 1) + (lane % 16)
-        // and tokens 4 (g >> 1) + r (first read) / 8 + 4 (g >> 1) + r (second read)
-        const int g = lane >> 4, i16 = lane & 15;
-        const int cv = (d0 >> 3) + 2 * (g & 1) + ((i16 & 3) >> 1);  // chunk for k-step 0 reads
-        const int tv = 4 * (g >> 1) + (i16 >> 2);
-        const int vb0 = slot_of(cv, tv) * 16 + 8 * (i16 & 1);
-        const int vb1 = slot_of(cv, tv + 8) * 16 + 8 * (i16 & 1);
+        const int v = w - 2, d0 = v * 256;
+        // Transposed V reads (ds_read_b64_tr_b16), 32x32x16 A operand of
+        // k-step kk, dim tile dt: 16-lane group g = lane / 16 covers dims
+        // d0 + 32 dt + 16 (g & 1) + (lane % 16); its lanes point at token
+        // 16 kk + 8 sel + 4 (g >> 1) + (lane % 16) / 4, 8 bytes at dim offset
+        // 4 (lane % 4), for sel = 0 (first read) and 1 (second read).
+        int vofs[2][2];  // [sel][dt & 1]; + 18432 kk + 1024 (dt / 2)
+        {
+            const int g = lane >> 4, i16 = lane & 15;
+            const int ta = 4 * (g >> 1) + (i16 >> 2);  // token within its group of 8
+            const int y2 = 2 * (g & 1) + ((i16 & 3) >> 1);
+#pragma unroll
+            for (int sel = 0; sel < 2; ++sel)
+#pragma unroll
+                for (int d1 = 0; d1 < 2; ++d1)
+                    vofs[sel][d1] = 9216 * sel + 4096 * v + 128 * ta +
+                                    16 * ((4 * d1) ^ y2 ^ swz(8 * sel + ta)) + 8 * (i16 & 1);
+        }
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
-            issue_step(sg, kv, 0, w, lane, ring0);
-            if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+            issue_step(sg, kv, 0, v, lane, ring0);
+            if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
             f32x16 o[2][8];
             bool again;
             do {  // one pass over the segment; repeated only after a restart
@@ -320,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         again = true;
                         break;
                     }
-                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, w, lane, ring0);
+                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, v, lane, ring0);
                     if (t == 0) continue;
                     const int tp = t - 1;  // half-page processed this step
                     const lds_u8 *V = smem + (tp % kRing) * kHalfBytes;
@@ -332,17 +371,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         bf16x8 vf[8];
     #pragma unroll
                         for (int dt = 0; dt < 8; ++dt) {
-                            // chunk advances by 4 per 32 dims, token by 16 per k-step; the
-                            // swizzle term depends only on chunk parity, which is unchanged
-                            const int off = dt * 4 * 32 * 16 + kk * 16 * 16;
+                            const int off = 18432 * kk + 1024 * (dt >> 1);
                             const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (i16x4 __attribute__((address_space(3))) *)(V + vb0 + off));
+                                (i16x4 __attribute__((address_space(3))) *)(V + vofs[0][dt & 1] + off));
                             const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (i16x4 __attribute__((address_space(3))) *)(V + vb1 + off));
+                                (i16x4 __attribute__((address_space(3))) *)(V + vofs[1][dt & 1] + off));
                             const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
                             vf[dt] = __builtin_bit_cast(bf16x8, v8);
                         }
-    #pragma unroll
+#pragma unroll
                         for (int dt = 0; dt < 8; ++dt) {
                             o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p0, o[0][dt], 0, 0, 0);
                             o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p1, o[1][dt], 0, 0, 0);
@@ -362,8 +399,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 if (again) {
                     wait_vmcnt<0>();
                     __syncthreads();
-                    issue_step(sg, kv, 0, w, lane, ring0);
-                    if (sg.H > 1) issue_step(sg, kv, 1, w, lane, ring0);
+                    issue_step(sg, kv, 0, v, lane, ring0);
+                    if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
                 }
             } while (again);
             __syncthreads();  // score waves' final stats visible
@@ -379,9 +416,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
                     for (int qd = 0; qd < 4; ++qd) {
-                        const f32x16 &v = o[r][dt];
+                        const f32x16 &acc = o[r][dt];
                         *(f32x4 *)(xrow + 32 * dt + 8 * qd) =
-                            (f32x4){v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]};
+                            (f32x4){acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
                     }
             }
             __syncthreads();  // staged output complete

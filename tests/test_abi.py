@@ -79,6 +79,9 @@ def _decode(lib, **kw):
     (dict(stride=0), INVALID),
     (dict(causal=2), INVALID),
     (dict(scale=float("nan")), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-0.04), INVALID),
+    (dict(scale=float("inf")), INVALID),
     (dict(h_q=8), UNSUPPORTED),
     (dict(h_q=48), UNSUPPORTED),
     (dict(s_q=3), UNSUPPORTED),
