@@ -56,26 +56,30 @@ __device__ __forceinline__ int swz(int tau) {
     return 4 * ((tau >> 1) & 1) + 2 * ((tau >> 2) & 1) + ((tau >> 3) & 1);
 }
 
-// Direct-to-LDS loads of value wave v's 18 of the 36 one-KB blocks of a
-// half-page: token groups 2v, 2v+1 (8 tokens each), line 0..8 of each row.
-// Lane l covers token 8 G + l / 8 and, within the 128-byte line, the chunk
-// whose swizzled slot is l % 8.  Tokens past tok_last re-read tok_last.
-__device__ __forceinline__ void issue_half(const unsigned char *kv, int64_t phys, int tok0,
-                                           int tok_last, int v, int lane, unsigned dst) {
+// Source row of value wave v's direct-to-LDS loads for token group G = 2 v + g2
+// of a half-page: lane l covers token 8 G + l / 8 (tokens past tok_last
+// re-read tok_last) and, within each 128-byte line, the chunk whose swizzled
+// slot is l % 8.
+__device__ __forceinline__ const unsigned char *dma_row(const unsigned char *kv, int64_t phys,
+                                                        int tok0, int tok_last, int v, int g2,
+                                                        int lane) {
     const int a = lane >> 3, b = lane & 7;
-#pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-        const int G = 2 * v + g2;
-        const int tau = 8 * G + a;
-        int t = tok0 + tau;
-        t = t < tok_last ? t : tok_last;
-        const unsigned char *src =
-            kv + (phys * kPage + t) * kTokBytesBf16 + 16 * (b ^ swz(tau));
-#pragma unroll
-        for (int lam = 0; lam < 9; ++lam)
-            dma16(src + 128 * lam, __builtin_amdgcn_readfirstlane(dst + (9 * G + lam) * 1024));
-    }
+    const int tau = 8 * (2 * v + g2) + a;
+    int t = tok0 + tau;
+    t = t < tok_last ? t : tok_last;
+    return kv + (phys * kPage + t) * kTokBytesBf16 + 16 * (b ^ swz(tau));
 }
+
+// Value wave v's share of a half-page: the 18 one-KB blocks (G, lam) with
+// G = 2 v + g2, each one 128-byte line (lam = 0..8) of eight tokens.
+struct HalfDma {
+    const unsigned char *src[2];  // per g2
+    unsigned dst;                 // LDS byte address of the half-page slot
+    __device__ __forceinline__ void issue(int v, int k) const {  // k = 9 g2 + lam
+        const int g2 = k / 9, lam = k % 9;
+        dma16(src[g2] + 128 * lam, __builtin_amdgcn_readfirstlane(dst + (9 * (2 * v + g2) + lam) * 1024));
+    }
+};
 
 // Both halves' maximum for lanes l and l ^ 32.
 __device__ __forceinline__ float max_xor32(float x) {
@@ -120,12 +124,24 @@ __device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int3
     }
 }
 
-// Direct-to-LDS loads of half-page t of a segment (value wave v's share).
-__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
-                                           int lane, unsigned ring0) {
+// Value wave v's direct-to-LDS loads of half-page t of a segment.
+__device__ __forceinline__ HalfDma half_dma(const Segment &sg, const unsigned char *kv, int t, int v,
+                                            int lane, unsigned ring0) {
     const int j = sg.j0 + (t >> 1);
     const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
-    issue_half(kv, sg.bt[j], (t & 1) * kHalf, tok_last, v, lane, ring0 + (t % kRing) * kHalfBytes);
+    const int64_t phys = sg.bt[j];
+    HalfDma d;
+    d.src[0] = dma_row(kv, phys, (t & 1) * kHalf, tok_last, v, 0, lane);
+    d.src[1] = dma_row(kv, phys, (t & 1) * kHalf, tok_last, v, 1, lane);
+    d.dst = ring0 + (t % kRing) * kHalfBytes;
+    return d;
+}
+
+__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
+                                           int lane, unsigned ring0) {
+    const HalfDma d = half_dma(sg, kv, t, v, lane, ring0);
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) d.issue(v, k);
 }
 
 // All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
@@ -228,11 +244,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 if (lane == 0) flag_lds[w] = 0;
                 for (int t = 0; t <= sg.H; ++t) {
                     __syncthreads();
-                    if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {  // restart with the larger reference
-                        again = true;
+                    // restart flags: read now, acted on after this step's MFMAs
+                    // (the value waves act on them at once; work done here in
+                    // the meantime is discarded)
+                    int f0 = flag_lds[0], f1 = flag_lds[1];
+                    if (t == sg.H) {
+                        again = __builtin_amdgcn_readfirstlane(f0 | f1) != 0;
                         break;
                     }
-                    if (t == sg.H) break;
                     const lds_u8 *S = smem + (t % kRing) * kHalfBytes;
                     f32x16 sacc = {};
                     constexpr int kPre = 8;  // K fragments in flight ahead of the MFMAs
@@ -256,6 +275,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+                    asm volatile("" : "+v"(f0), "+v"(f1));  // keeps the flag test behind the MFMAs
+                    if (__builtin_amdgcn_readfirstlane(f0 | f1)) {  // restart with the larger reference
+                        again = true;
+                        break;
+                    }
                     // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row
                     const int tok0 = sg.j0 * kPage + t * kHalf;
                     float x[16];
@@ -359,42 +383,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         again = true;
                         break;
                     }
-                    if (t + 2 < sg.H) issue_step(sg, kv, t + 2, v, lane, ring0);
-                    if (t == 0) continue;
+                    const bool more = t + 2 < sg.H;
+                    if (t == 0) {
+                        if (more) issue_step(sg, kv, t + 2, v, lane, ring0);
+                        continue;
+                    }
+                    // Half-page t + 2 goes to the slot half-page t - 2 used; its
+                    // loads are spread over this step's MFMAs (one per MFMA
+                    // pair) so that no load waits for the memory pipeline.
                     const int tp = t - 1;  // half-page processed this step
                     const lds_u8 *V = smem + (tp % kRing) * kHalfBytes;
                     const lds_u8 *P = smem + kPOff + (tp & 1) * kPBytes;
-    #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const bf16x8 p0 = *(const bf16x8 __attribute__((address_space(3))) *)(P + (0 + kk) * 1024 + lane * 16);
-                        const bf16x8 p1 = *(const bf16x8 __attribute__((address_space(3))) *)(P + (2 + kk) * 1024 + lane * 16);
-                        bf16x8 vf[8];
-    #pragma unroll
-                        for (int dt = 0; dt < 8; ++dt) {
-                            const int off = 18432 * kk + 1024 * (dt >> 1);
-                            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (i16x4 __attribute__((address_space(3))) *)(V + vofs[0][dt & 1] + off));
-                            const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (i16x4 __attribute__((address_space(3))) *)(V + vofs[1][dt & 1] + off));
-                            const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-                            vf[dt] = __builtin_bit_cast(bf16x8, v8);
-                        }
+                    HalfDma dma;
+                    if (more) dma = half_dma(sg, kv, t + 2, v, lane, ring0);
+                    auto read_v = [&](int kk, int dt) {
+                        const int off = 18432 * kk + 1024 * (dt >> 1);
+                        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (i16x4 __attribute__((address_space(3))) *)(V + vofs[0][dt & 1] + off));
+                        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (i16x4 __attribute__((address_space(3))) *)(V + vofs[1][dt & 1] + off));
+                        const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+                        return __builtin_bit_cast(bf16x8, v8);
+                    };
+                    auto read_p = [&](int blk) {
+                        return *(const bf16x8 __attribute__((address_space(3))) *)(P + blk * 1024 + lane * 16);
+                    };
+                    // k-step 0: all its operands first; k-step 1's operands are
+                    // read between k-step 0's MFMAs, one DMA after each MFMA pair
+                    bf16x8 v0[8], v1[8];
+                    const bf16x8 p00 = read_p(0), p01 = read_p(2);
 #pragma unroll
-                        for (int dt = 0; dt < 8; ++dt) {
-                            o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p0, o[0][dt], 0, 0, 0);
-                            o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], p1, o[1][dt], 0, 0, 0);
-                        }
-                    }
-                    // overlap reads and MFMAs: the first k-step's P and V reads,
-                    // then two MFMAs per two reads, then the remaining MFMAs
-                    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+                    for (int dt = 0; dt < 8; ++dt) v0[dt] = read_v(0, dt);
+                    const bf16x8 p10 = read_p(1), p11 = read_p(3);
 #pragma unroll
-                    for (int k = 0; k < 13; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    for (int dt = 0; dt < 8; ++dt) {
+                        o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p00, o[0][dt], 0, 0, 0);
+                        o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p01, o[1][dt], 0, 0, 0);
+                        v1[dt] = read_v(1, dt);
+                        if (more) dma.issue(v, dt);
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) {
+                        o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p10, o[0][dt], 0, 0, 0);
+                        o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p11, o[1][dt], 0, 0, 0);
+                        if (more) dma.issue(v, 8 + dt);
+                    }
+                    if (more) {
+#pragma unroll
+                        for (int k = 16; k < kDmaPerWave; ++k) dma.issue(v, k);
+                    }
                 }
                 if (again) {
                     wait_vmcnt<0>();

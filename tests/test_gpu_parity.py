@@ -50,6 +50,26 @@ def test_shapes_with_poisoned_tails_match_oracle(seqlens, s_q, h_q, causal, fp8)
     compare(out, lse, ref_out, ref_lse, f"{seqlens} s_q={s_q} h_q={h_q} causal={causal} fp8={fp8}")
 
 
+GROWING = [
+    # seqlens, s_q, h_q, causal, num_parts: RoPE keys scaled up along the
+    # sequence, so each row's running max keeps rising (the 16-row kernel
+    # rescales, the 64-row kernel restarts segments)
+    ([300, 1000, 2100], 1, 128, False, 8),
+    ([1000, 3000], 2, 64, True, 4),
+    ([300, 1000, 2100], 2, 16, True, 8),
+    ([300, 1000, 2100], 1, 128, False, 64),
+]
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal,num_parts", GROWING)
+def test_growing_scores_match_oracle(seqlens, s_q, h_q, causal, num_parts):
+    case = W.make_case(seqlens, s_q, h_q, seed=12 + h_q, causal=causal, spare_pages=1, poison=True,
+                       rope_ramp=0.05)
+    out, lse = run_gpu(case, num_parts=num_parts)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, f"growing {seqlens} s_q={s_q} h_q={h_q} parts={num_parts}")
+
+
 @pytest.mark.parametrize("num_parts", [1, 7, 64, 256, 1024])
 def test_result_does_not_depend_on_the_split(num_parts):
     case = W.make_case([900, 33, 2000, 64], 2, 32, seed=7, causal=True, spare_pages=2, poison=True)

@@ -90,8 +90,12 @@ class Case:
 
 
 def make_case(seqlens, s_q, h_q, seed, causal=False, fp8=False, spare_pages=0, poison=False,
-              permute=True, scale=None, name="", rng=None):
-    """Build a Case.  ``seqlens`` is a sequence of ints (already drawn)."""
+              permute=True, scale=None, name="", rng=None, rope_ramp=0.0):
+    """Build a Case.  ``seqlens`` is a sequence of ints (already drawn).
+
+    ``rope_ramp`` > 0 multiplies the 64 RoPE dims of the key at position j by
+    (1 + rope_ramp * j): scores then grow along the sequence (a running max
+    that keeps rising) while the 512 value dims keep unit scale."""
     if rng is None:
         rng = np.random.Generator(np.random.PCG64(seed))
     seqlens = np.asarray(seqlens, dtype=np.int32)
@@ -108,7 +112,10 @@ def make_case(seqlens, s_q, h_q, seed, causal=False, fp8=False, spare_pages=0, p
     logical = []
     for b in range(batch):
         n_tok = pages[b] * PAGE
-        vals = bf16_bits(rng.standard_normal((n_tok, D_QK), dtype=np.float32))
+        raw = rng.standard_normal((n_tok, D_QK), dtype=np.float32)
+        if rope_ramp:
+            raw[:, D_V:] *= (1.0 + rope_ramp * np.arange(n_tok, dtype=np.float32))[:, None]
+        vals = bf16_bits(raw)
         if fp8:
             vals = quantize_fp8_records(vals)
         logical.append(vals.reshape(pages[b], PAGE, *rec_shape))
