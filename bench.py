@@ -97,24 +97,36 @@ class Runner:
             raise RuntimeError(f"libmla call failed in {self.name}")
 
     def measure(self, steps, warmup):
+        """Times `steps` whole steps between two events (nothing else inside
+        the timed region), then, in a second pass of `steps` steps, the plan,
+        attention and combine calls separately with events on the same
+        stream."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = e0.elapsed_time(e1) / steps
+        wall_ms_step = (t1 - t0) * 1e3 / steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         for k in range(steps):
             self.step(evs[k])
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_step = (t1 - t0) * 1e3 / steps
         plan = np.mean([e[0].elapsed_time(e[1]) for e in evs])
         attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
         comb = np.mean([e[2].elapsed_time(e[3]) for e in evs])
         n_split = int(self.split_base[-1].item())
-        return dict(ms_per_step=ms_step, plan_us=plan * 1e3, attn_us=attn * 1e3,
-                    combine_us=comb * 1e3, split_slots=n_split)
+        return dict(ms_per_step=ms_step, wall_ms_per_step=wall_ms_step, plan_us=plan * 1e3,
+                    attn_us=attn * 1e3, combine_us=comb * 1e3, split_slots=n_split)
 
     def report(self, m):
         s = m["ms_per_step"] * 1e-3
@@ -123,7 +135,8 @@ class Runner:
         gbs_k, tfl_k = self.bytes / a / 1e9, self.flops / a / 1e12
         bound = "hbm" if self.bytes / (PEAK_HBM_GBS * 1e9) >= self.flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
         return dict(
-            us_per_step=round(m["ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
+            us_per_step=round(m["ms_per_step"] * 1e3, 2),
+            wall_us_per_step=round(m["wall_ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
             attn_us=round(m["attn_us"], 2), combine_us=round(m["combine_us"], 2),
             split_slots=m["split_slots"], num_parts=self.num_parts,
             alg_bytes=self.bytes, alg_flops=self.flops,

@@ -13,6 +13,7 @@ void plan_host(const int32_t *seqlens, int batch, int c, int num_parts, int32_t 
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 int decode_rows_per_group();
 hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -25,7 +26,7 @@ namespace {
 
 // Kernel choice: 64 query rows per work-group with specialised score / value
 // waves when a request has at least 64 rows; 16 rows per work-group otherwise.
-bool use_rows64(int kv_format, int M) { return kv_format == 0 && M >= 64; }
+bool use_rows64(int M) { return M >= 64; }
 
 bool shape_supported(int s_q, int h_q) {
     return (s_q == 1 || s_q == 2) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
@@ -84,9 +85,10 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
     hipError_t e;
-    if (use_rows64(kv_format, M)) {
+    if (use_rows64(M)) {
         a.row_groups = M / 64;
-        e = mla::launch_decode_rows64(a, (hipStream_t)stream);
+        e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
+                           : mla::launch_decode_rows64(a, (hipStream_t)stream);
     } else {
         a.row_groups = M / mla::decode_rows_per_group();
         e = mla::launch_decode(a, kv_format == 1, (hipStream_t)stream);
@@ -153,7 +155,7 @@ int mla_default_num_parts(int device, int s_q, int h_q) {
     // kernel and M / 16 (run in several rounds) in the 16-row kernel
     const int M = s_q * h_q;
     int parts = g_cu_count[device];
-    if (use_rows64(0, M)) parts = parts / (M / 64);
+    if (use_rows64(M)) parts = parts / (M / 64);
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
 }

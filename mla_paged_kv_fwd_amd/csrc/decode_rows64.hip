@@ -28,28 +28,21 @@
 
 #include "common.h"
 #include "device_util.h"
+#include "rows64.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsWG = 64;                       // query rows per work-group
-constexpr int kHalf = 32;                         // tokens per step
+using namespace rows64;
+
 constexpr int kHalfBytes = kHalf * kTokBytesBf16;  // 36864
-constexpr int kRing = 4;
 constexpr int kDmaPerWave = kHalfBytes / 1024 / 2;  // 18 direct-to-LDS loads per value wave per step
 constexpr int kPOff = kRing * kHalfBytes;         // P hand-off: 2 x (2 row tiles x 2 k-steps x 1 KB)
 constexpr int kPBytes = 4096;
 constexpr int kFlagOff = kPOff + 2 * kPBytes;     // restart flags of the two score waves
 constexpr int kStatOff = kFlagOff + 64;           // final (m, l) per row
 constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
-constexpr float kGrowLog2 = 16.f;  // reference headroom (log2 units) before a segment restarts
-constexpr int kXStride = kDV + 4;                 // padded row stride of the output stage
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // XOR term of the half-page layout for token tau (bits 1, 2, 3 of tau).
 __device__ __forceinline__ int swz(int tau) {
@@ -81,49 +74,6 @@ struct HalfDma {
     }
 };
 
-// Both halves' maximum for lanes l and l ^ 32.
-__device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_own_dma(bool more) {
-    if (more) wait_vmcnt<N>(); else wait_vmcnt<0>();
-}
-
-// One request segment of a part: pages j0..j1 of request b.
-struct Segment {
-    int b, L, npages, j0, rank, nsplit, H;  // H = number of 32-token steps
-    const int32_t *bt;
-};
-
-// Calls f(seg) for every non-empty request segment of a part, in order.
-template <class F>
-__device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int32_t *seqlens,
-                                                 const int32_t *split_base,
-                                                 const int32_t *block_table, int64_t bt_stride,
-                                                 F &&f) {
-    const int b_first = mrow[0], j_first = mrow[1], b_last = mrow[2], j_last = mrow[3];
-    for (int b = b_first; b <= b_last; ++b) {
-        Segment sg;
-        sg.b = b;
-        sg.L = seqlens[b];
-        if (sg.L <= 0) continue;
-        sg.npages = (sg.L + kPage - 1) / kPage;
-        sg.j0 = (b == b_first) ? j_first : 0;
-        const int j1 = (b == b_last) ? j_last : sg.npages - 1;
-        sg.rank = (b == b_first) ? mrow[4] : 0;
-        sg.nsplit = split_base[b + 1] - split_base[b];
-        sg.bt = block_table + (int64_t)b * bt_stride;
-        // the last page may hold a single half
-        const int tok_end = (j1 == sg.npages - 1) ? sg.L : (j1 + 1) * kPage;
-        sg.H = (tok_end - sg.j0 * kPage + kHalf - 1) / kHalf;
-        f(sg);
-    }
-}
-
 // Value wave v's direct-to-LDS loads of half-page t of a segment.
 __device__ __forceinline__ HalfDma half_dma(const Segment &sg, const unsigned char *kv, int t, int v,
                                             int lane, unsigned ring0) {
@@ -142,35 +92,6 @@ __device__ __forceinline__ void issue_step(const Segment &sg, const unsigned cha
     const HalfDma d = half_dma(sg, kv, t, v, lane, ring0);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) d.issue(v, k);
-}
-
-// All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
-// segment's split slot (fp32), four threads per row, coalesced.
-__device__ __forceinline__ void write_rows(const DecodeArgs &a, const Segment &sg,
-                                           const int32_t *split_base, const float *X,
-                                           const float *row_sum, int row0, int tid) {
-    const int r = tid >> 2, c0 = (tid & 3) * 128;
-    const int orow = row0 + r;
-    const float *xr = X + r * kXStride + c0;
-    const float lsum = row_sum[r];
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    if (sg.nsplit == 1) {
-        uint16_t *dst = a.out + ((int64_t)sg.b * a.M + orow) * kDV + c0;
-#pragma unroll 4
-        for (int d = 0; d < 128; d += 8) {
-            const f32x4 u0 = *(const f32x4 *)(xr + d) * inv, u1 = *(const f32x4 *)(xr + d + 4) * inv;
-            u32x4 pk;
-            pk[0] = (unsigned)f32_to_bf16_bits(u0[0]) | ((unsigned)f32_to_bf16_bits(u0[1]) << 16);
-            pk[1] = (unsigned)f32_to_bf16_bits(u0[2]) | ((unsigned)f32_to_bf16_bits(u0[3]) << 16);
-            pk[2] = (unsigned)f32_to_bf16_bits(u1[0]) | ((unsigned)f32_to_bf16_bits(u1[1]) << 16);
-            pk[3] = (unsigned)f32_to_bf16_bits(u1[2]) | ((unsigned)f32_to_bf16_bits(u1[3]) << 16);
-            *(u32x4 *)(dst + d) = pk;
-        }
-    } else {
-        float *dst = a.o_part + ((int64_t)(split_base[sg.b] + sg.rank) * a.M + orow) * kDV + c0;
-#pragma unroll 4
-        for (int d = 0; d < 128; d += 4) *(f32x4 *)(dst + d) = *(const f32x4 *)(xr + d) * inv;
-    }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
@@ -363,18 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
             f32x16 o[2][8];
             bool again;
             do {  // one pass over the segment; repeated only after a restart
-                // Zero the accumulators with MFMAs (0 x 0 + 0) so they are born
-                // in the accumulator registers; plain zero stores get hoisted
-                // into 256 VGPRs of constants by the compiler.
-                u32x4 zw;
-                asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
-                             : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
-                const bf16x8 zf = __builtin_bit_cast(bf16x8, zw);
-#pragma unroll
-                for (int r = 0; r < 2; ++r)
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-                        o[r][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, (f32x16){}, 0, 0, 0);
+                zero_acc(o);
                 again = false;
                 for (int t = 0; t <= sg.H; ++t) {
                     wait_own_dma<kDmaPerWave>(t + 1 < sg.H);
@@ -441,23 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 }
             } while (again);
             __syncthreads();  // score waves' final stats visible
-            // Stage O^T (unnormalised fp32) in LDS as [row][dim]; the ring is free.
-            // Plain stores straight from the accumulators (no arithmetic), so
-            // no accumulator tile has to pass through VGPRs.
-            // lane holds, for row tile r, row 32 r + lane % 32 and dims
-            // d0 + 32 dt + 8 (i / 4) + 4 h + (i % 4)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                float *xrow = X + (32 * r + l32) * kXStride + d0 + 4 * h;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const f32x16 &acc = o[r][dt];
-                        *(f32x4 *)(xrow + 32 * dt + 8 * qd) =
-                            (f32x4){acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
-                    }
-            }
+            stage_output(X, o, d0, lane);  // the ring is free
             __syncthreads();  // staged output complete
             write_rows(a, sg, split_base, X, stat_lds + kRowsWG, row0, tid);
             __syncthreads();  // LDS free for the next segment

@@ -1,0 +1,377 @@
+// MLA decode attention over an FP8 latent cache for many query rows per
+// request (s_q * h_q >= 64): gfx950 kernel with specialised waves.
+//
+// Cache record (656 bytes per token): 512 OCP E4M3FN codes of the latent
+// dims, four little-endian fp32 scales (one per 128-dim tile), 64 bf16 RoPE
+// dims.  The dequantised key is code * scale[dim / 128].
+//
+// Work split as in the bf16 64-row kernel: a work-group of 4 waves owns one
+// split part and 64 query rows, walking the part in 32-token half-pages;
+// waves 0, 1 score 32 rows each, waves 2, 3 accumulate 256 output dims each
+// for all 64 rows, one half-page behind, and issue all loads.
+//
+// Dequantisation happens in registers, exactly:
+//   - a K fragment (8 codes of one token) is read with ds_read_b64 and turned
+//     into bf16 with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (every E4M3FN
+//     value is a bf16 value); QK^T keeps one accumulator per 128-dim tile plus
+//     one for the RoPE dims, and the token's tile scales weight the tile
+//     accumulators afterwards, in fp32;
+//   - a V fragment (one dim of 8 tokens) comes from ds_read_b64_tr_b8; each
+//     code is widened to fp32, multiplied by its token's tile scale and
+//     rounded once to bf16 (P stays the plain bf16 softmax weight, as in the
+//     bf16 kernel, so the largest weight of a row is exact).
+//
+// A half-page (32 records, 20992 bytes) lands in LDS as the plain memory
+// image, 21 direct-to-LDS loads of 1 KB each; records past the segment's last
+// token are replaced by that token's record.  With a 656-byte record stride
+// (164 dwords, 36 mod 64 banks) both the ds_read_b64 K reads of 16 tokens and
+// the transposed V reads of 8 tokens hit distinct banks, so no swizzle is
+// needed.
+#include <math.h>
+
+#include "common.h"
+#include "device_util.h"
+#include "rows64.h"
+
+namespace mla {
+
+namespace {
+
+using namespace rows64;
+
+constexpr int kHalfFp8 = kHalf * kTokBytesFp8;         // 20992
+constexpr int kDmaFp8 = (kHalfFp8 + 1023) / 1024;      // 21 one-KB loads per half-page
+constexpr int kDmaWave = (kDmaFp8 + 1) / 2;            // 11 per value wave: blocks 0..10 and 10..20
+constexpr int kSlot = kDmaFp8 * 1024;                  // 21504 (the last load is half padding)
+constexpr int kChunks = kTokBytesFp8 / 16;             // 41 sixteen-byte chunks per record
+constexpr int kPOff = kRing * kSlot;                   // 86016
+constexpr int kPBytes = 4096;                          // P^T: 2 row tiles x 2 k-steps x 1 KB
+constexpr int kXBytes = kRowsWG * kXStride * 4;        // output stage, over ring and P
+constexpr int kFlagOff = (kPOff + 2 * kPBytes) > kXBytes ? (kPOff + 2 * kPBytes) : kXBytes;
+constexpr int kStatOff = kFlagOff + 64;
+constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// 8 E4M3FN codes (little-endian in two dwords) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 codes_to_bf16(unsigned lo, unsigned hi) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Value wave v's direct-to-LDS loads of a half-page: 1 KB block i covers
+// bytes [1024 i, 1024 i + 1024) of the 32 records; lane l takes chunk
+// 64 i + l, moved to the same chunk of record tok_last when it lies past it.
+struct HalfDmaFp8 {
+    const unsigned char *hp;  // first record of the half-page
+    unsigned dst;             // LDS byte address of the slot
+    int tok_last;
+    __device__ __forceinline__ void issue(int i, int lane) const {
+        int ch = 64 * i + lane;
+        const int tau = ch / kChunks;
+        if (tau > tok_last) ch = kChunks * tok_last + (ch - kChunks * tau);
+        dma16(hp + 16 * ch, __builtin_amdgcn_readfirstlane(dst + 1024 * i));
+    }
+};
+
+__device__ __forceinline__ HalfDmaFp8 half_dma(const Segment &sg, const unsigned char *kv, int t,
+                                               unsigned ring0) {
+    const int j = sg.j0 + (t >> 1);
+    HalfDmaFp8 d;
+    d.hp = kv + ((int64_t)sg.bt[j] * kPage + (t & 1) * kHalf) * kTokBytesFp8;
+    d.dst = ring0 + (t % kRing) * kSlot;
+    d.tok_last = sg.tok_last(t);
+    return d;
+}
+
+// Blocks of value wave v: 0 .. 10 (v = 0) or 10 .. 20 (v = 1).  Both waves
+// load block 10 (the same bytes to the same place), which keeps their code
+// identical.
+__device__ __forceinline__ int first_block(int v) { return v ? kDmaFp8 - kDmaWave : 0; }
+
+__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
+                                           int lane, unsigned ring0) {
+    const HalfDmaFp8 d = half_dma(sg, kv, t, ring0);
+#pragma unroll
+    for (int k = 0; k < kDmaWave; ++k) d.issue(first_block(v) + k, lane);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
+    const DecodeArgs a, const uint16_t *__restrict__ q, const unsigned char *__restrict__ kv,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ seqlens,
+    const int32_t *__restrict__ meta, const int32_t *__restrict__ split_base) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kLdsBytes];
+    lds_u8 *smem = (lds_u8 *)smem_raw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // blockIdx -> (part, row group), row groups of a part on one XCD
+    const int lin = blockIdx.x;
+    const int rest = lin >> 3;
+    const int rg = rest % a.row_groups;
+    const int part = (rest / a.row_groups) * 8 + (lin & 7);
+    if (part >= a.num_parts) return;
+    const int32_t *mrow = meta + part * kMetaInts;
+    if (mrow[0] < 0) return;
+
+    const unsigned ring0 = lds_addr(smem);
+    volatile __attribute__((address_space(3))) int *flag_lds =
+        (volatile __attribute__((address_space(3))) int *)(smem + kFlagOff);
+    float *stat_lds = (float *)(smem_raw + kStatOff);
+    float *X = (float *)smem_raw;  // output stage [64][kXStride]
+    const int row0 = rg * kRowsWG;
+
+    if (w < 2) {
+        // ================= score waves: rows row0 + 32 w + (lane % 32)
+        const int row = row0 + 32 * w + l32;
+        const int qi = row / a.h_q;
+        const float c = a.scale_log2;  // > 0
+        const float grow = kGrowLog2 / c;
+        const int krec = kTokBytesFp8 * l32;  // this lane's K token record in a slot
+        for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
+            n_visible = n_visible > 0 ? n_visible : 0;
+            const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;
+            // Q^T operand for 32x32x16: lane holds dims 16 ks + 8 h .. +8 of its row
+            bf16x8 qf[kDQk / 16];
+            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row) * kDQk + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < kDQk / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+#pragma unroll
+            for (int ks = 0; ks < kDQk / 16; ++ks) asm volatile("" : : "v"(qf[ks]));
+            float m_seen = -INFINITY, m, lsum;
+            bool again;
+            do {  // one pass over the segment; repeated only after a restart
+                m = m_seen;
+                lsum = 0.f;
+                again = false;
+                bool ovf = false;
+                if (lane == 0) flag_lds[w] = 0;
+                for (int t = 0; t <= sg.H; ++t) {
+                    __syncthreads();
+                    int f0 = flag_lds[0], f1 = flag_lds[1];
+                    if (t == sg.H) {
+                        again = __builtin_amdgcn_readfirstlane(f0 | f1) != 0;
+                        break;
+                    }
+                    const lds_u8 *S = smem + (t % kRing) * kSlot;
+                    // S^T (32 tokens x 32 rows) per 128-dim tile and for the RoPE dims
+                    f32x16 acc[5] = {};
+                    constexpr int kPre = 8;
+                    u32x2 kc[kPre];
+#pragma unroll
+                    for (int ks = 0; ks < kPre; ++ks) kc[ks] = *(const lds_u32x2 *)(S + krec + 16 * ks + 8 * h);
+                    bf16x8 kr[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        kr[r] = *(const lds_bf16x8 *)(S + krec + kFp8RopeAt + 32 * r + 16 * h);
+#pragma unroll
+                    for (int ks = 0; ks < 32; ++ks) {
+                        const u32x2 cur = kc[ks % kPre];
+                        if (ks + kPre < 32) kc[ks % kPre] = *(const lds_u32x2 *)(S + krec + 16 * (ks + kPre) + 8 * h);
+                        acc[ks >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_to_bf16(cur[0], cur[1]),
+                                                                               qf[ks], acc[ks >> 3], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[r], qf[32 + r], acc[4], 0, 0, 0);
+                    asm volatile("" : "+v"(f0), "+v"(f1));  // the flag test stays behind the MFMAs
+                    if (__builtin_amdgcn_readfirstlane(f0 | f1)) {
+                        again = true;
+                        break;
+                    }
+                    // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row;
+                    // their tile scales sit at byte 512 of each record
+                    auto scales = [&](int i) {
+                        return *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt);
+                    };
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const f32x4 sc = scales(i);
+                        x[i] = acc[4][i] + sc[0] * acc[0][i] + sc[1] * acc[1][i] + sc[2] * acc[2][i] +
+                               sc[3] * acc[3][i];
+                    }
+                    const int tok0 = sg.j0 * kPage + t * kHalf;
+                    if (tok0 + kHalf > n_visible_all) {  // the causal edge or the segment's end
+                        const int tok_base = tok0 + 4 * h;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            x[i] = (tok_base + 8 * (i >> 2) + (i & 3) < n_visible) ? x[i] : -INFINITY;
+                    }
+                    float mloc = x[0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+                    mloc = max_xor32(mloc);
+                    m_seen = fmaxf(m_seen, mloc);
+                    if (m == -INFINITY) m = mloc;  // first keys of this row
+                    ovf |= mloc > m + grow;
+                    flag_lds[w] = __builtin_amdgcn_ballot_w64(ovf) != 0;  // same value from every lane
+                    const float mc = (m == -INFINITY) ? 0.f : m * c;
+                    float p[16], psum = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -mc));
+                        psum += p[i];
+                    }
+                    lsum += psum;
+                    // P^T operand blocks: (row tile w, k-step kk) -> 1 KB at P + (2 w + kk) KB
+                    lds_u8 *P = smem + kPOff + (t & 1) * kPBytes + (2 * w) * 1024 + lane * 16;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int i0 = 8 * kk;
+                        *(lds_u32x4 *)(P + kk * 1024) =
+                            (u32x4){pack_bf16(p[i0], p[i0 + 1]), pack_bf16(p[i0 + 2], p[i0 + 3]),
+                                    pack_bf16(p[i0 + 4], p[i0 + 5]), pack_bf16(p[i0 + 6], p[i0 + 7])};
+                    }
+                }
+                if (again) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                }
+            } while (again);
+            lsum += __shfl_xor(lsum, 32);
+            if (h == 0) {
+                stat_lds[kRowsWG + 32 * w + l32] = lsum;
+                const float lse_val =
+                    lsum > 0.f ? (m * c + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
+                if (sg.nsplit == 1)
+                    a.lse[(int64_t)sg.b * a.M + row] = lse_val;
+                else
+                    a.lse_part[(int64_t)(split_base[sg.b] + sg.rank) * a.M + row] = lse_val;
+            }
+            __syncthreads();  // stats visible to the value waves
+            __syncthreads();  // value waves have staged the output
+            write_rows(a, sg, split_base, X, stat_lds + kRowsWG, row0, tid);
+            __syncthreads();  // LDS free for the next segment
+        });
+    } else {
+        // ================= value waves: dims d0 .. d0 + 255 (tiles 2 v, 2 v + 1), all 64 rows
+        const int v = w - 2, d0 = v * 256;
+        // Transposed V reads (ds_read_b64_tr_b8), 32x32x16 A operand of
+        // k-step kk, dim tile dt.  The k order must match P^T, which keeps the
+        // score accumulator's order: lane half h = lane / 32 holds tokens
+        // 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step.  16-lane group
+        // g = lane / 16 covers dims d0 + 32 dt + 16 (g & 1) + (lane % 16); its
+        // lanes 2 r, 2 r + 1 point at the r-th of those 8 tokens, 8 codes at
+        // dim offset 8 (lane % 2).
+        const int g = lane >> 4, i16 = lane & 15, vr = i16 >> 1;
+        const int vtok = 4 * (g >> 1) + (vr & 3) + 8 * (vr >> 2);
+        const int vrec = kTokBytesFp8 * vtok + d0 + 16 * (g & 1) + 8 * (i16 & 1);
+        // scales of tiles 2 v, 2 v + 1 of this lane's first token (4 (lane / 32))
+        const int vsc = kTokBytesFp8 * (4 * (lane >> 5)) + kFp8ScalesAt + 8 * v;
+        for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            issue_step(sg, kv, 0, v, lane, ring0);
+            if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+            f32x16 o[2][8];
+            bool again;
+            do {  // one pass over the segment; repeated only after a restart
+                zero_acc(o);
+                again = false;
+                for (int t = 0; t <= sg.H; ++t) {
+                    wait_own_dma<kDmaWave>(t + 1 < sg.H);
+                    __syncthreads();
+                    if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {
+                        again = true;  // the score waves restart the segment
+                        break;
+                    }
+                    const bool more = t + 2 < sg.H;
+                    if (t == 0) {
+                        if (more) issue_step(sg, kv, t + 2, v, lane, ring0);
+                        continue;
+                    }
+                    // half-page t + 2 goes to the slot half-page t - 2 used; its
+                    // loads are spread over this step's MFMAs (one after each
+                    // MFMA pair)
+                    HalfDmaFp8 dma;
+                    if (more) dma = half_dma(sg, kv, t + 2, ring0);
+                    const int i0 = first_block(v);
+                    const int tp = t - 1;  // half-page processed this step
+                    const lds_u8 *V = smem + (tp % kRing) * kSlot + vrec;
+                    const lds_u8 *Vs = smem + (tp % kRing) * kSlot + vsc;
+                    const lds_u8 *P = smem + kPOff + (tp & 1) * kPBytes + lane * 16;
+                    // scales of this lane's 8 tokens of k-step kk (tile 2 v and 2 v + 1)
+                    auto read_scales = [&](int kk, f32x2 (&sc)[8]) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            sc[j] = *(const lds_f32x2 *)(Vs + kTokBytesFp8 * (16 * kk + (j & 3) + 8 * (j >> 2)));
+                    };
+                    // V^T fragment: one dim of the 8 tokens, each code times its
+                    // token's scale of tile 2 v + (dt / 4), rounded to bf16
+                    auto read_v = [&](int kk, int dt, const f32x2 (&sc)[8]) {
+                        const i32x2 cv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                            (lds_i32x2 *)(V + kTokBytesFp8 * 16 * kk + 32 * dt));
+                        const int ti = dt >> 2;
+                        const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((unsigned)cv[0], false);
+                        const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((unsigned)cv[0], true);
+                        const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((unsigned)cv[1], false);
+                        const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((unsigned)cv[1], true);
+                        return __builtin_bit_cast(bf16x8, (u32x4){
+                            pack_bf16(a0[0] * sc[0][ti], a0[1] * sc[1][ti]), pack_bf16(a1[0] * sc[2][ti], a1[1] * sc[3][ti]),
+                            pack_bf16(a2[0] * sc[4][ti], a2[1] * sc[5][ti]), pack_bf16(a3[0] * sc[6][ti], a3[1] * sc[7][ti])});
+                    };
+                    auto read_p = [&](int r, int kk) {
+                        return *(const lds_bf16x8 *)(P + (2 * r + kk) * 1024);
+                    };
+                    // k-step 0's operands first; k-step 1's are read between
+                    // k-step 0's MFMAs
+                    f32x2 sc0[8], sc1[8];
+                    read_scales(0, sc0);
+                    bf16x8 v0[8], v1[8];
+                    const bf16x8 p00 = read_p(0, 0), p10 = read_p(1, 0);
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) v0[dt] = read_v(0, dt, sc0);
+                    read_scales(1, sc1);
+                    const bf16x8 p01 = read_p(0, 1), p11 = read_p(1, 1);
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) {
+                        o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p00, o[0][dt], 0, 0, 0);
+                        o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p10, o[1][dt], 0, 0, 0);
+                        v1[dt] = read_v(1, dt, sc1);
+                        if (more) dma.issue(i0 + dt, lane);
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) {
+                        o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p01, o[0][dt], 0, 0, 0);
+                        o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p11, o[1][dt], 0, 0, 0);
+                    if (more && dt < kDmaWave - 8) dma.issue(i0 + 8 + dt, lane);
+                    }
+                }
+                if (again) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    issue_step(sg, kv, 0, v, lane, ring0);
+                    if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+                }
+            } while (again);
+            __syncthreads();  // score waves' final stats visible
+            stage_output(X, o, d0, lane);
+            __syncthreads();  // staged output complete
+            write_rows(a, sg, split_base, X, stat_lds + kRowsWG, row0, tid);
+            __syncthreads();  // LDS free for the next segment
+        });
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream) {
+    const int groups8 = (a.num_parts + 7) / 8;
+    const dim3 grid(groups8 * 8 * a.row_groups), block(kThreads);
+    hipLaunchKernelGGL(decode_rows64_fp8_kernel, grid, block, 0, stream, a, a.q, a.kv,
+                       a.block_table, a.seqlens, a.meta, a.split_base);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,137 @@
+// Pieces shared by the 64-row decode kernels (bf16 and FP8 caches): the
+// work-group shape, request segments of a split part, the softmax restart
+// threshold and the output epilogue.
+#pragma once
+
+#include "common.h"
+#include "device_util.h"
+
+namespace mla {
+namespace rows64 {
+
+constexpr int kThreads = 256;   // 4 waves: 2 score waves, 2 value waves
+constexpr int kRowsWG = 64;     // query rows per work-group
+constexpr int kHalf = 32;       // tokens per step (half a page)
+constexpr int kRing = 4;        // half-pages resident in LDS
+constexpr float kGrowLog2 = 16.f;  // reference headroom (log2 units) before a segment restarts
+constexpr int kXStride = kDV + 4;  // padded row stride of the output stage
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Both halves' maximum for lanes l and l ^ 32.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_own_dma(bool more) {
+    if (more) wait_vmcnt<N>(); else wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// One request segment of a part: pages j0..j1 of request b.
+struct Segment {
+    int b, L, npages, j0, rank, nsplit, H;  // H = number of 32-token steps
+    const int32_t *bt;
+    // last valid token (0..31) of half-page t of the segment
+    __device__ __forceinline__ int tok_last(int t) const {
+        const int first = (j0 + (t >> 1)) * kPage + (t & 1) * kHalf;
+        const int last = L - 1 - first;
+        return last < kHalf - 1 ? last : kHalf - 1;
+    }
+};
+
+// Calls f(seg) for every non-empty request segment of a part, in order.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int32_t *seqlens,
+                                                 const int32_t *split_base,
+                                                 const int32_t *block_table, int64_t bt_stride,
+                                                 F &&f) {
+    const int b_first = mrow[0], j_first = mrow[1], b_last = mrow[2], j_last = mrow[3];
+    for (int b = b_first; b <= b_last; ++b) {
+        Segment sg;
+        sg.b = b;
+        sg.L = seqlens[b];
+        if (sg.L <= 0) continue;
+        sg.npages = (sg.L + kPage - 1) / kPage;
+        sg.j0 = (b == b_first) ? j_first : 0;
+        const int j1 = (b == b_last) ? j_last : sg.npages - 1;
+        sg.rank = (b == b_first) ? mrow[4] : 0;
+        sg.nsplit = split_base[b + 1] - split_base[b];
+        sg.bt = block_table + (int64_t)b * bt_stride;
+        // the last page may hold a single half
+        const int tok_end = (j1 == sg.npages - 1) ? sg.L : (j1 + 1) * kPage;
+        sg.H = (tok_end - sg.j0 * kPage + kHalf - 1) / kHalf;
+        f(sg);
+    }
+}
+
+// All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
+// segment's split slot (fp32), four threads per row, coalesced.
+__device__ __forceinline__ void write_rows(const DecodeArgs &a, const Segment &sg,
+                                           const int32_t *split_base, const float *X,
+                                           const float *row_sum, int row0, int tid) {
+    const int r = tid >> 2, c0 = (tid & 3) * 128;
+    const int orow = row0 + r;
+    const float *xr = X + r * kXStride + c0;
+    const float lsum = row_sum[r];
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (sg.nsplit == 1) {
+        uint16_t *dst = a.out + ((int64_t)sg.b * a.M + orow) * kDV + c0;
+#pragma unroll 4
+        for (int d = 0; d < 128; d += 8) {
+            const f32x4 u0 = *(const f32x4 *)(xr + d) * inv, u1 = *(const f32x4 *)(xr + d + 4) * inv;
+            *(u32x4 *)(dst + d) = (u32x4){pack_bf16(u0[0], u0[1]), pack_bf16(u0[2], u0[3]),
+                                          pack_bf16(u1[0], u1[1]), pack_bf16(u1[2], u1[3])};
+        }
+    } else {
+        float *dst = a.o_part + ((int64_t)(split_base[sg.b] + sg.rank) * a.M + orow) * kDV + c0;
+#pragma unroll 4
+        for (int d = 0; d < 128; d += 4) *(f32x4 *)(dst + d) = *(const f32x4 *)(xr + d) * inv;
+    }
+}
+
+// Stage O^T (unnormalised fp32, 2 row tiles x 8 dim tiles of 32x32) of the
+// value wave owning dims d0 .. d0 + 255 in LDS as [row][dim].  Lane holds,
+// for row tile r, row 32 r + lane % 32 and dims d0 + 32 dt + 8 (i / 4) +
+// 4 (lane / 32) + (i % 4).  Plain stores straight from the accumulators.
+__device__ __forceinline__ void stage_output(float *X, const f32x16 (&o)[2][8], int d0, int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        float *xrow = X + (32 * r + l32) * kXStride + d0 + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x16 &acc = o[r][dt];
+                *(f32x4 *)(xrow + 32 * dt + 8 * qd) =
+                    (f32x4){acc[4 * qd], acc[4 * qd + 1], acc[4 * qd + 2], acc[4 * qd + 3]};
+            }
+    }
+}
+
+// Zeroes the accumulators with MFMAs (0 x 0 + 0), so they are born in the
+// accumulator registers; plain zero stores get hoisted into 256 VGPRs of
+// constants by the compiler.
+__device__ __forceinline__ void zero_acc(f32x16 (&o)[2][8]) {
+    u32x4 zw;
+    asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                 : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
+    const bf16x8 zf = __builtin_bit_cast(bf16x8, zw);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            o[r][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, (f32x16){}, 0, 0, 0);
+}
+
+}  // namespace rows64
+}  // namespace mla

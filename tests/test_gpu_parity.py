@@ -38,6 +38,8 @@ SHAPES = [
     ([1, 63, 64, 65, 200, 1000], 1, 16, False, True),
     ([2, 65, 300], 2, 32, True, True),
     ([5, 64, 257], 1, 128, False, True),
+    ([1, 31, 32, 33, 63, 64, 65, 700], 1, 64, False, True),
+    ([2, 66, 130, 400], 2, 128, True, True),
 ]
 
 
@@ -51,23 +53,26 @@ def test_shapes_with_poisoned_tails_match_oracle(seqlens, s_q, h_q, causal, fp8)
 
 
 GROWING = [
-    # seqlens, s_q, h_q, causal, num_parts: RoPE keys scaled up along the
+    # seqlens, s_q, h_q, causal, num_parts, fp8: RoPE keys scaled up along the
     # sequence, so each row's running max keeps rising (the 16-row kernel
-    # rescales, the 64-row kernel restarts segments)
-    ([300, 1000, 2100], 1, 128, False, 8),
-    ([1000, 3000], 2, 64, True, 4),
-    ([300, 1000, 2100], 2, 16, True, 8),
-    ([300, 1000, 2100], 1, 128, False, 64),
+    # rescales, the 64-row kernels restart segments)
+    ([300, 1000, 2100], 1, 128, False, 8, False),
+    ([1000, 3000], 2, 64, True, 4, False),
+    ([300, 1000, 2100], 2, 16, True, 8, False),
+    ([300, 1000, 2100], 1, 128, False, 64, False),
+    ([300, 1000, 2100], 1, 128, False, 8, True),
+    ([1000, 3000], 2, 32, True, 4, True),
 ]
 
 
-@pytest.mark.parametrize("seqlens,s_q,h_q,causal,num_parts", GROWING)
-def test_growing_scores_match_oracle(seqlens, s_q, h_q, causal, num_parts):
-    case = W.make_case(seqlens, s_q, h_q, seed=12 + h_q, causal=causal, spare_pages=1, poison=True,
-                       rope_ramp=0.05)
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal,num_parts,fp8", GROWING)
+def test_growing_scores_match_oracle(seqlens, s_q, h_q, causal, num_parts, fp8):
+    case = W.make_case(seqlens, s_q, h_q, seed=12 + h_q, causal=causal, fp8=fp8, spare_pages=1,
+                       poison=True, rope_ramp=0.05)
     out, lse = run_gpu(case, num_parts=num_parts)
     ref_out, ref_lse = oracle_all(case)
-    compare(out, lse, ref_out, ref_lse, f"growing {seqlens} s_q={s_q} h_q={h_q} parts={num_parts}")
+    compare(out, lse, ref_out, ref_lse,
+            f"growing {seqlens} s_q={s_q} h_q={h_q} parts={num_parts} fp8={fp8}")
 
 
 @pytest.mark.parametrize("num_parts", [1, 7, 64, 256, 1024])
