@@ -219,10 +219,10 @@ def roofline(rep, workload):
 
     cfg = W.CONFIGS[workload]
     rows = cfg["s_q"] * cfg["h_q"]
-    if cfg["fp8"] or rows < 64:
+    if rows < 64:
         kernel = "decode_rowgroup_kernel<%s>" % ("true" if cfg["fp8"] else "false")
     else:
-        kernel = "decode_rows64_kernel"
+        kernel = "decode_rows64_fp8_kernel" if cfg["fp8"] else "decode_rows64_kernel"
     traffic = measured_traffic(kernel, workload)
     if rep["bound"] == "hbm":
         achieved, peak, unit = rep["attn_gbs"], PEAK_HBM_GBS, "GB/s"

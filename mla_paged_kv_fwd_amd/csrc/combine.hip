@@ -30,30 +30,46 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int d = (threadIdx.x & 63) * 8;
     uint16_t *dst = out + ((int64_t)b * M + r) * kDV + d;
 
+    // Every slot's lse and partial output are loaded up front, four slots at a
+    // time, so that the loads of a request overlap instead of waiting on one
+    // another.  A slot with lse = -inf gets weight 0 whatever it holds.
+    const float *lrow = lse_part + (int64_t)base * M + r;
+    const float *orow = o_part + ((int64_t)base * M + r) * kDV + d;
+    const int64_t ostride = (int64_t)M * kDV;
     float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lse_part[(int64_t)(base + s) * M + r]);
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lrow[(int64_t)s * M]);
     if (mx == -INFINITY) {  // no pages, or no visible key in any slot
         *(u32x4 *)dst = (u32x4){0u, 0u, 0u, 0u};
         if (d == 0) lse[(int64_t)b * M + r] = -INFINITY;
         return;
     }
     float z = 0.f;
-    for (int s = 0; s < ns; ++s) z += expf(lse_part[(int64_t)(base + s) * M + r] - mx);
-    const float lse_all = mx + logf(z);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-        const float ls = lse_part[(int64_t)(base + s) * M + r];
-        if (ls == -INFINITY) continue;
-        const float wgt = expf(ls - lse_all);
-        const float *src = o_part + ((int64_t)(base + s) * M + r) * kDV + d;
-        const f32x4 v0 = *(const f32x4 *)src;
-        const f32x4 v1 = *(const f32x4 *)(src + 4);
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+        float ls[4];
+        f32x4 v0[4], v1[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[e] += wgt * v0[e];
-            acc[4 + e] += wgt * v1[e];
+        for (int k = 0; k < 4; ++k) {
+            const int s = s0 + k < ns ? s0 + k : ns - 1;
+            ls[k] = s0 + k < ns ? lrow[(int64_t)s * M] : -INFINITY;
+            v0[k] = *(const f32x4 *)(orow + s * ostride);
+            v1[k] = *(const f32x4 *)(orow + s * ostride + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float e = expf(ls[k] - mx);  // 0 for an empty slot
+            z += e;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[j] += ls[k] == -INFINITY ? 0.f : e * v0[k][j];
+                acc[4 + j] += ls[k] == -INFINITY ? 0.f : e * v1[k][j];
+            }
         }
     }
+    const float lse_all = mx + logf(z);
+    const float inv_z = 1.f / z;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv_z;
     unsigned pk[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)

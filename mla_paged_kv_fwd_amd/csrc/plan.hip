@@ -9,22 +9,44 @@ namespace mla {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 
-// Block-wide exclusive scan of one int per thread (kPlanThreads threads).
-__device__ int block_exclusive_scan(int v, int *scratch, int *total) {
-    const int t = threadIdx.x;
-    scratch[t] = v;
+// Inclusive prefix sum across the 64 lanes of a wave with row shifts and row
+// broadcasts (DPP): sums within each 16-lane row, then row 0's total into row
+// 1 and row 2's into row 3, then lanes 0..31's total into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// Block-wide inclusive scan of two ints per thread: a scan within each wave,
+// then every thread adds the totals of the waves before it.  Two barriers.
+// *total receives the block-wide sums.
+__device__ int2 block_inclusive_scan2(int2 v, int2 *wave_tot, int2 *total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    v.x = wave_inclusive_scan(v.x);
+    v.y = wave_inclusive_scan(v.y);
+    if (lane == 63) wave_tot[wv] = v;
     __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        int add = (t >= off) ? scratch[t - off] : 0;
-        __syncthreads();
-        scratch[t] += add;
-        __syncthreads();
+    int2 pre = {0, 0}, tot = {0, 0};
+#pragma unroll
+    for (int k = 0; k < kPlanWaves; ++k) {
+        const int2 w = wave_tot[k];
+        if (k < wv) {
+            pre.x += w.x;
+            pre.y += w.y;
+        }
+        tot.x += w.x;
+        tot.y += w.y;
     }
-    int incl = scratch[t];
-    *total = scratch[kPlanThreads - 1];
-    __syncthreads();
-    return incl - v;
+    __syncthreads();  // wave_tot may be reused
+    *total = tot;
+    return {v.x + pre.x, v.y + pre.y};
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *__restrict__ seqlens,
@@ -33,32 +55,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *__res
                                                             int32_t *__restrict__ split_base) {
     __shared__ int32_t pages_pre[kMaxBatch + 1];
     __shared__ int32_t nonempty_pre[kMaxBatch + 1];
-    __shared__ int scratch[kPlanThreads];
+    __shared__ int2 wave_tot[kPlanWaves];
     const int t = threadIdx.x;
+    // thread t owns requests b_lo .. b_hi - 1; their page counts wait in
+    // pages_pre until the scan has produced the offsets
     const int chunk = (batch + kPlanThreads - 1) / kPlanThreads;
     const int b_lo = min(batch, t * chunk), b_hi = min(batch, b_lo + chunk);
 
-    int my_pages = 0, my_nonempty = 0;
+    int2 mine = {0, 0};  // (pages, non-empty requests)
     for (int b = b_lo; b < b_hi; ++b) {
-        int L = seqlens[b];
-        int n = L > 0 ? (L + kPage - 1) / kPage : 0;
-        my_pages += n;
-        my_nonempty += n > 0;
+        const int L = seqlens[b];
+        const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+        pages_pre[b] = n;
+        mine.x += n;
+        mine.y += n > 0;
     }
-    int tot_pages, tot_nonempty;
-    int pages_off = block_exclusive_scan(my_pages, scratch, &tot_pages);
-    int ne_off = block_exclusive_scan(my_nonempty, scratch, &tot_nonempty);
+    int2 tot;
+    const int2 incl = block_inclusive_scan2(mine, wave_tot, &tot);
+    int pages_off = incl.x - mine.x, ne_off = incl.y - mine.y;
     for (int b = b_lo; b < b_hi; ++b) {
+        const int n = pages_pre[b];
         pages_pre[b] = pages_off;
         nonempty_pre[b] = ne_off;
-        int L = seqlens[b];
-        int n = L > 0 ? (L + kPage - 1) / kPage : 0;
         pages_off += n;
         ne_off += n > 0;
     }
     if (t == 0) {
-        pages_pre[batch] = tot_pages;
-        nonempty_pre[batch] = tot_nonempty;
+        pages_pre[batch] = tot.x;
+        nonempty_pre[batch] = tot.y;
     }
     __syncthreads();
 
@@ -67,7 +91,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *__res
     v.nonempty_pre = nonempty_pre;
     v.batch = batch;
     v.c = c;
-    v.total = (int64_t)tot_pages + (int64_t)c * tot_nonempty;
+    v.total = (int64_t)tot.x + (int64_t)c * tot.y;
     v.parts_eff = v.total < num_parts ? v.total : num_parts;
 
     for (int p = t; p < num_parts; p += kPlanThreads) {
@@ -76,15 +100,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t *__res
         for (int k = 0; k < kMetaInts; ++k) meta[p * kMetaInts + k] = row[k];
     }
 
-    int my_splits = 0;
-    for (int b = b_lo; b < b_hi; ++b) my_splits += v.splits_of(b);
-    int tot_splits;
-    int off = block_exclusive_scan(my_splits, scratch, &tot_splits);
+    int2 my_splits = {0, 0};
+    for (int b = b_lo; b < b_hi; ++b) my_splits.x += v.splits_of(b);
+    int2 tot_splits;
+    int off = block_inclusive_scan2(my_splits, wave_tot, &tot_splits).x - my_splits.x;
     for (int b = b_lo; b < b_hi; ++b) {
         split_base[b] = off;
         off += v.splits_of(b);
     }
-    if (t == 0) split_base[batch] = tot_splits;
+    if (t == 0) split_base[batch] = tot_splits.x;
 }
 
 }  // namespace

@@ -97,7 +97,8 @@ def test_gpu_plan_equals_oracle_plan():
 
     rng = np.random.default_rng(3)
     cases = [([37, 100], 1, 16, 8), ([4096] * 128, 1, 16, 256), ([131072] * 8, 1, 128, 256),
-             ([0, 5, 0, 0, 64, 65, 0], 2, 32, 7), ([1], 1, 16, 1024), ([0, 0], 1, 16, 8)]
+             ([0, 5, 0, 0, 64, 65, 0], 2, 32, 7), ([1], 1, 16, 1024), ([0, 0], 1, 16, 8),
+             (list(rng.integers(0, 3000, size=16384)), 1, 16, 4096), ([64] * 1025, 1, 64, 333)]
     for _ in range(10):
         n = int(rng.integers(1, 3000))
         cases.append((list(rng.integers(0, 9000, size=n)), int(rng.choice([1, 2])),
