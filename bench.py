@@ -30,7 +30,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
     p.add_argument("--extra", default="computebound,fp8,longctx",
                    help="comma list of further workloads to measure ('' for none)")

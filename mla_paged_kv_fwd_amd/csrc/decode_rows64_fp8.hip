@@ -168,21 +168,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     const lds_u8 *S = smem + (t % kRing) * kSlot;
                     // S^T (32 tokens x 32 rows) per 128-dim tile and for the RoPE dims
                     f32x16 acc[5] = {};
-                    constexpr int kPre = 8;
-                    u32x2 kc[kPre];
-#pragma unroll
-                    for (int ks = 0; ks < kPre; ++ks) kc[ks] = *(const lds_u32x2 *)(S + krec + 16 * ks + 8 * h);
+                    // K codes of k-steps 2 pp, 2 pp + 1 (8 bytes each), kPairs
+                    // pairs in flight ahead of their MFMAs; the fences pin
+                    // that order
+                    constexpr int kPairs = 4;
+                    auto read_pair = [&](int pp) {
+                        const u32x2 a = *(const lds_u32x2 *)(S + krec + 32 * pp + 8 * h);
+                        const u32x2 b = *(const lds_u32x2 *)(S + krec + 32 * pp + 16 + 8 * h);
+                        return (u32x4){a[0], a[1], b[0], b[1]};
+                    };
                     bf16x8 kr[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         kr[r] = *(const lds_bf16x8 *)(S + krec + kFp8RopeAt + 32 * r + 16 * h);
+                    u32x4 kc[kPairs];
 #pragma unroll
-                    for (int ks = 0; ks < 32; ++ks) {
-                        const u32x2 cur = kc[ks % kPre];
-                        if (ks + kPre < 32) kc[ks % kPre] = *(const lds_u32x2 *)(S + krec + 16 * (ks + kPre) + 8 * h);
-                        acc[ks >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_to_bf16(cur[0], cur[1]),
-                                                                               qf[ks], acc[ks >> 3], 0, 0, 0);
+                    for (int pp = 0; pp < kPairs; ++pp) kc[pp] = read_pair(pp);
+#pragma unroll
+                    for (int pp = 0; pp < 16; ++pp) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        const u32x4 cur = kc[pp % kPairs];
+                        if (pp + kPairs < 16) kc[pp % kPairs] = read_pair(pp + kPairs);
+                        f32x16 &at = acc[pp >> 2];
+                        at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_to_bf16(cur[0], cur[1]), qf[2 * pp], at, 0, 0, 0);
+                        at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(codes_to_bf16(cur[2], cur[3]), qf[2 * pp + 1], at, 0, 0, 0);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         acc[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[r], qf[32 + r], acc[4], 0, 0, 0);
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     for (int dt = 0; dt < 8; ++dt) {
                         o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p01, o[0][dt], 0, 0, 0);
                         o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p11, o[1][dt], 0, 0, 0);
-                    if (more && dt < kDmaWave - 8) dma.issue(i0 + 8 + dt, lane);
+                        if (more && dt < kDmaWave - 8) dma.issue(i0 + 8 + dt, lane);
                     }
                 }
                 if (again) {
