@@ -163,10 +163,14 @@ def measured_traffic(kernel, workload):
                 fields[k.strip()] = v.strip()
         if fields.get("traffic_kernel") != kernel or fields.get("traffic_workload") != workload:
             continue
-        src = os.path.join(here, fields.get("traffic_source", ""))
-        if not os.path.isfile(src):
-            return None
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("traffic_source_sha256"):
+        # the profiled sources: one sha256 over their bytes in the listed order
+        h = hashlib.sha256()
+        for rel in fields.get("traffic_source", "").split():
+            src = os.path.join(here, rel)
+            if not os.path.isfile(src):
+                return None
+            h.update(open(src, "rb").read())
+        if h.hexdigest() != fields.get("traffic_source_sha256"):
             return None
         return int(fields["traffic_bytes_per_launch"])
     return None
