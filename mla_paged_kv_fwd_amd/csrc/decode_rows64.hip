@@ -162,13 +162,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 m = m_seen;
                 lsum = 0.f;
                 again = false;
-                if (lane == 0) flag_lds[w] = 0;
+                // Restart flags by step parity: in step t a score wave writes slot
+                // t % 2, and every wave reads slot (t + 1) % 2 (written in step
+                // t - 1) right after the step's barrier, so no flag is read in
+                // the step that writes it.
+                if (lane == 0) {
+                    flag_lds[w] = 0;
+                    flag_lds[2 + w] = 0;
+                }
                 for (int t = 0; t <= sg.H; ++t) {
                     __syncthreads();
                     // restart flags: read now, acted on after this step's MFMAs
                     // (the value waves act on them at once; work done here in
                     // the meantime is discarded)
-                    int f0 = flag_lds[0], f1 = flag_lds[1];
+                    const int fr = 2 * ((t + 1) & 1);
+                    int f0 = flag_lds[fr], f1 = flag_lds[fr + 1];
                     if (t == sg.H) {
                         again = __builtin_amdgcn_readfirstlane(f0 | f1) != 0;
                         break;
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     m_seen = fmaxf(m_seen, mloc);
                     if (m == -INFINITY) m = mloc;  // first keys of this row
                     const bool overflow = mloc > m + grow;
-                    if (__builtin_amdgcn_ballot_w64(overflow) != 0 && lane == 0) flag_lds[w] = 1;
+                    flag_lds[2 * (t & 1) + w] = __builtin_amdgcn_ballot_w64(overflow) != 0;  // same value from every lane
                     const float mc = (m == -INFINITY) ? 0.f : m * c;
                     float psum = 0.f;
                     unsigned pk[8];
@@ -289,7 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 for (int t = 0; t <= sg.H; ++t) {
                     wait_own_dma<kDmaPerWave>(t + 1 < sg.H);
                     __syncthreads();
-                    if (__builtin_amdgcn_readfirstlane(flag_lds[0] | flag_lds[1])) {  // the score waves restart the segment
+                    const int fr = 2 * ((t + 1) & 1);
+                    if (__builtin_amdgcn_readfirstlane(flag_lds[fr] | flag_lds[fr + 1])) {  // the score waves restart the segment
                         again = true;
                         break;
                     }
