@@ -211,17 +211,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         break;
                     }
                     // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row;
-                    // their tile scales sit at byte 512 of each record
-                    auto scales = [&](int i) {
-                        return *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt);
-                    };
-                    float x[16];
+                    // their tile scales sit at byte 512 of each record.  One tile's 16
+                    // scales are read while the previous tile's are applied, the order
+                    // pinned by fences, so the LDS latency is paid about once.
+                    auto tile_scales = [&](int k, float (&sc)[16]) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const f32x4 sc = scales(i);
-                        x[i] = acc[4][i] + sc[0] * acc[0][i] + sc[1] * acc[1][i] + sc[2] * acc[2][i] +
-                               sc[3] * acc[3][i];
-                    }
+                        for (int i = 0; i < 16; ++i)
+                            sc[i] = *(const __attribute__((address_space(3))) float *)(
+                                S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt + 4 * k);
+                    };
+                    float x[16], scA[16], scB[16];
+                    __builtin_amdgcn_sched_barrier(0);
+                    tile_scales(0, scA);
+                    __builtin_amdgcn_sched_barrier(0);
+                    tile_scales(1, scB);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[i] = acc[4][i] + scA[i] * acc[0][i];
+                    __builtin_amdgcn_sched_barrier(0);
+                    tile_scales(2, scA);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[i] += scB[i] * acc[1][i];
+                    __builtin_amdgcn_sched_barrier(0);
+                    tile_scales(3, scB);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[i] += scA[i] * acc[2][i];
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[i] += scB[i] * acc[3][i];
+                    __builtin_amdgcn_sched_barrier(0);
                     const int tok0 = sg.j0 * kPage + t * kHalf;
                     if (tok0 + kHalf > n_visible_all) {  // the causal edge or the segment's end
                         const int tok_base = tok0 + 4 * h;
