@@ -13,7 +13,10 @@ constexpr int kThreads = 256;   // 4 waves: 2 score waves, 2 value waves
 constexpr int kRowsWG = 64;     // query rows per work-group
 constexpr int kHalf = 32;       // tokens per step (half a page)
 constexpr int kRing = 4;        // half-pages resident in LDS
-constexpr float kGrowLog2 = 16.f;  // reference headroom (log2 units) before a segment restarts
+// Reference headroom (log2 units) before a segment restarts.  Weights up to
+// 2^64 stay exact in bf16's exponent range and their sums over any sequence
+// stay far below fp32's, so a large headroom only makes restarts rarer.
+constexpr float kGrowLog2 = 64.f;
 constexpr int kXStride = kDV + 4;  // padded row stride of the output stage
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
