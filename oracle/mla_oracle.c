@@ -2,7 +2,7 @@
  * MLA paged-KV decode oracle -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, obviously correct CPU definition of what the decode path
- * computes, used to judge the GPU library.  Only the tests, the smoke check
+ * computes, used to check the GPU library.  Only the tests, the smoke check
  * and the benchmark's CPU-baseline leg may load this file's library.  It shares
  * no code, header, table or constant with the HIP library.
  *
