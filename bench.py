@@ -98,9 +98,10 @@ class Runner:
 
     def measure(self, steps, warmup):
         """Times `steps` whole steps between two events (nothing else inside
-        the timed region), then, in a second pass of `steps` steps, the plan,
+        the timed region); then, in a second pass of `steps` steps, the plan,
         attention and combine calls separately with events on the same
-        stream."""
+        stream; then `steps` attention launches back to back between two
+        events (the kernel's average launch duration, the roofline's time)."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
@@ -124,13 +125,22 @@ class Runner:
         plan = np.mean([e[0].elapsed_time(e[1]) for e in evs])
         attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
         comb = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(steps):
+            if self.lib.mla_decode_attn(*self._attn_args, stream.cuda_stream) != 0:
+                raise RuntimeError(f"libmla call failed in {self.name}")
+        a1.record(stream)
+        torch.cuda.synchronize()
+        kernel = a0.elapsed_time(a1) / steps
         n_split = int(self.split_base[-1].item())
         return dict(ms_per_step=ms_step, wall_ms_per_step=wall_ms_step, plan_us=plan * 1e3,
-                    attn_us=attn * 1e3, combine_us=comb * 1e3, split_slots=n_split)
+                    attn_us=attn * 1e3, combine_us=comb * 1e3, attn_kernel_us=kernel * 1e3,
+                    split_slots=n_split)
 
     def report(self, m):
         s = m["ms_per_step"] * 1e-3
-        a = m["attn_us"] * 1e-6
+        a = m["attn_kernel_us"] * 1e-6
         gbs, tfl = self.bytes / s / 1e9, self.flops / s / 1e12
         gbs_k, tfl_k = self.bytes / a / 1e9, self.flops / a / 1e12
         bound = "hbm" if self.bytes / (PEAK_HBM_GBS * 1e9) >= self.flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
@@ -138,6 +148,7 @@ class Runner:
             us_per_step=round(m["ms_per_step"] * 1e3, 2),
             wall_us_per_step=round(m["wall_ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
             attn_us=round(m["attn_us"], 2), combine_us=round(m["combine_us"], 2),
+            attn_kernel_us=round(m["attn_kernel_us"], 2),
             split_slots=m["split_slots"], num_parts=self.num_parts,
             alg_bytes=self.bytes, alg_flops=self.flops,
             gbs=round(gbs, 1), tflops=round(tfl, 1),
