@@ -75,6 +75,31 @@ def test_growing_scores_match_oracle(seqlens, s_q, h_q, causal, num_parts, fp8):
             f"growing {seqlens} s_q={s_q} h_q={h_q} parts={num_parts} fp8={fp8}")
 
 
+WIDE = [
+    # seqlens, s_q, h_q, causal, fp8: query rows scaled by their own power of
+    # two and a quarter of their entries made 2^12 smaller (the FP8 kernels
+    # split each query row into two E4M3 halves under a per-row scale)
+    ([5, 64, 257, 700], 1, 128, False, True),
+    ([2, 66, 130, 400], 2, 64, True, True),
+    ([300, 64], 1, 16, False, True),
+    ([5, 64, 257], 1, 128, False, False),
+]
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal,fp8", WIDE)
+def test_wide_range_queries_match_oracle(seqlens, s_q, h_q, causal, fp8):
+    case = W.make_case(seqlens, s_q, h_q, seed=40 + h_q, causal=causal, fp8=fp8, spare_pages=1,
+                       poison=True)
+    rng = np.random.default_rng(41 + h_q)
+    rows = (case.q.astype(np.uint32) << 16).view(np.float32).reshape(-1, case.q.shape[-1]).copy()
+    rows *= np.exp2(rng.integers(-12, 6, size=(rows.shape[0], 1))).astype(np.float32)
+    rows[rng.random(rows.shape) < 0.25] *= np.float32(2.0 ** -12)
+    case.q = W.bf16_bits(rows.reshape(case.q.shape))
+    out, lse = run_gpu(case)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, f"wide queries {seqlens} s_q={s_q} h_q={h_q} fp8={fp8}")
+
+
 @pytest.mark.parametrize("num_parts", [1, 7, 64, 256, 1024])
 def test_result_does_not_depend_on_the_split(num_parts):
     case = W.make_case([900, 33, 2000, 64], 2, 32, seed=7, causal=True, spare_pages=2, poison=True)
