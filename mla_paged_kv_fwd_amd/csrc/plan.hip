@@ -8,7 +8,7 @@ namespace mla {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // Inclusive prefix sum across the 64 lanes of a wave with row shifts and row
