@@ -15,19 +15,12 @@
 // during step t the score waves read half-page t, the value waves half-page
 // t-1, and half-pages t+1, t+2 are in flight.  One work-group barrier per step.
 //
-// Half-page LDS layout (36 KB, 2304 slots of 16 bytes).  Token tau (0..31),
-// 16-byte chunk c (0..71) of its 1152-byte row sits in slot
-//   64 * (9 * (tau / 8) + c / 8) + 8 * (tau % 8) + ((c % 8) ^ swz(tau)),
-//   swz(tau) = 4 * bit1(tau) + 2 * bit2(tau) + bit3(tau).
-// Each 1 KB block holds one 128-byte line of eight consecutive tokens, so a
-// direct-to-LDS load reads eight whole cache lines; the XOR keeps the K
-// operand reads (ds_read_b128, 16 lanes per LDS cycle) and the transposed V
-// operand reads (ds_read_b64_tr_b16, 16 or 32 lanes per cycle) free of bank
-// conflicts.
+// The half-page LDS layout and the operand addressing are in halfpage_bf16.h.
 #include <math.h>
 
 #include "common.h"
 #include "device_util.h"
+#include "halfpage_bf16.h"
 #include "rows64.h"
 
 namespace mla {
@@ -36,32 +29,13 @@ namespace {
 
 using namespace rows64;
 
-constexpr int kHalfBytes = kHalf * kTokBytesBf16;  // 36864
+constexpr int kHalfBytes = halfpage::kBytes;  // 36864
 constexpr int kDmaPerWave = kHalfBytes / 1024 / 2;  // 18 direct-to-LDS loads per value wave per step
 constexpr int kPOff = kRing * kHalfBytes;         // P hand-off: 2 x (2 row tiles x 2 k-steps x 1 KB)
 constexpr int kPBytes = 4096;
 constexpr int kFlagOff = kPOff + 2 * kPBytes;     // restart flags of the two score waves
 constexpr int kStatOff = kFlagOff + 64;           // final (m, l) per row
 constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
-
-// XOR term of the half-page layout for token tau (bits 1, 2, 3 of tau).
-__device__ __forceinline__ int swz(int tau) {
-    return 4 * ((tau >> 1) & 1) + 2 * ((tau >> 2) & 1) + ((tau >> 3) & 1);
-}
-
-// Source row of value wave v's direct-to-LDS loads for token group G = 2 v + g2
-// of a half-page: lane l covers token 8 G + l / 8 (tokens past tok_last
-// re-read tok_last) and, within each 128-byte line, the chunk whose swizzled
-// slot is l % 8.
-__device__ __forceinline__ const unsigned char *dma_row(const unsigned char *kv, int64_t phys,
-                                                        int tok0, int tok_last, int v, int g2,
-                                                        int lane) {
-    const int a = lane >> 3, b = lane & 7;
-    const int tau = 8 * (2 * v + g2) + a;
-    int t = tok0 + tau;
-    t = t < tok_last ? t : tok_last;
-    return kv + (phys * kPage + t) * kTokBytesBf16 + 16 * (b ^ swz(tau));
-}
 
 // Value wave v's share of a half-page: the 18 one-KB blocks (G, lam) with
 // G = 2 v + g2, each one 128-byte line (lam = 0..8) of eight tokens.
@@ -81,8 +55,8 @@ __device__ __forceinline__ HalfDma half_dma(const Segment &sg, const unsigned ch
     const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
     const int64_t phys = sg.bt[j];
     HalfDma d;
-    d.src[0] = dma_row(kv, phys, (t & 1) * kHalf, tok_last, v, 0, lane);
-    d.src[1] = dma_row(kv, phys, (t & 1) * kHalf, tok_last, v, 1, lane);
+    d.src[0] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v, lane);
+    d.src[1] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v + 1, lane);
     d.dst = ring0 + (t % kRing) * kHalfBytes;
     return d;
 }
@@ -130,15 +104,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         const int qi = row / a.h_q;
         const float c = a.scale_log2;  // > 0
         const float grow = kGrowLog2 / c;
-        // K operand of k-step ks for this lane: token lane % 32, chunk 2 ks + h,
-        // at kofs[ks % 4] + 1024 (ks / 4) in the half-page
-        int kofs[4];
-        {
-            const int tau = l32, y = h ^ swz(tau);
-#pragma unroll
-            for (int k3 = 0; k3 < 4; ++k3)
-                kofs[k3] = 9216 * (tau >> 3) + 128 * (tau & 7) + 16 * ((2 * k3) ^ y);
-        }
+        int kofs[4];  // K operand of k-step ks for this lane
+        halfpage::k_offsets(kofs, l32, h);
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
             int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
             n_visible = n_visible > 0 ? n_visible : 0;
@@ -187,13 +154,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     bf16x8 kf[kPre];
 #pragma unroll
                     for (int ks = 0; ks < kPre; ++ks)
-                        kf[ks] = *(const bf16x8 __attribute__((address_space(3))) *)(S + kofs[ks & 3] + 1024 * (ks >> 2));
+                        kf[ks] = halfpage::read_k(S, kofs, ks);
 #pragma unroll
                     for (int ks = 0; ks < kDQk / 16; ++ks) {
                         const bf16x8 cur = kf[ks % kPre];
                         const int kn = ks + kPre;
                         if (kn < kDQk / 16)
-                            kf[ks % kPre] = *(const bf16x8 __attribute__((address_space(3))) *)(S + kofs[kn & 3] + 1024 * (kn >> 2));
+                            kf[ks % kPre] = halfpage::read_k(S, kofs, kn);
                         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc, 0, 0, 0);
                     }
                     // keep kPre K reads in flight: kPre reads, then one MFMA per read
@@ -269,23 +236,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
     } else {
         // ================= value waves: dims d0 .. d0 + 255 for all 64 rows
         const int v = w - 2, d0 = v * 256;
-        // Transposed V reads (ds_read_b64_tr_b16), 32x32x16 A operand of
-        // k-step kk, dim tile dt: 16-lane group g = lane / 16 covers dims
-        // d0 + 32 dt + 16 (g & 1) + (lane % 16); its lanes point at token
-        // 16 kk + 8 sel + 4 (g >> 1) + (lane % 16) / 4, 8 bytes at dim offset
-        // 4 (lane % 4), for sel = 0 (first read) and 1 (second read).
-        int vofs[2][2];  // [sel][dt & 1]; + 18432 kk + 1024 (dt / 2)
-        {
-            const int g = lane >> 4, i16 = lane & 15;
-            const int ta = 4 * (g >> 1) + (i16 >> 2);  // token within its group of 8
-            const int y2 = 2 * (g & 1) + ((i16 & 3) >> 1);
-#pragma unroll
-            for (int sel = 0; sel < 2; ++sel)
-#pragma unroll
-                for (int d1 = 0; d1 < 2; ++d1)
-                    vofs[sel][d1] = 9216 * sel + 4096 * v + 128 * ta +
-                                    16 * ((4 * d1) ^ y2 ^ swz(8 * sel + ta)) + 8 * (i16 & 1);
-        }
+        int vofs[2][2];  // transposed V reads of this wave's 256 dims
+        halfpage::v_offsets(vofs, lane, 4 * v);
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
             issue_step(sg, kv, 0, v, lane, ring0);
             if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
@@ -315,15 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     const lds_u8 *P = smem + kPOff + (tp & 1) * kPBytes;
                     HalfDma dma;
                     if (more) dma = half_dma(sg, kv, t + 2, v, lane, ring0);
-                    auto read_v = [&](int kk, int dt) {
-                        const int off = 18432 * kk + 1024 * (dt >> 1);
-                        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (i16x4 __attribute__((address_space(3))) *)(V + vofs[0][dt & 1] + off));
-                        const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (i16x4 __attribute__((address_space(3))) *)(V + vofs[1][dt & 1] + off));
-                        const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-                        return __builtin_bit_cast(bf16x8, v8);
-                    };
+                    auto read_v = [&](int kk, int dt) { return halfpage::read_v(V, vofs, kk, dt); };
                     auto read_p = [&](int blk) {
                         return *(const bf16x8 __attribute__((address_space(3))) *)(P + blk * 1024 + lane * 16);
                     };

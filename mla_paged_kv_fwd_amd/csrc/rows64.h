@@ -20,7 +20,6 @@ constexpr float kGrowLog2 = 64.f;
 constexpr int kXStride = kDV + 4;  // padded row stride of the output stage
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Both halves' maximum for lanes l and l ^ 32.
