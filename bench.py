@@ -56,7 +56,7 @@ class Runner:
         self.batch = seqlens.shape[0]
         self.bytes = W.algorithmic_bytes(seqlens, self.s_q, self.h_q, self.fp8)
         self.flops = W.algorithmic_flops(seqlens, self.s_q, self.h_q, self.causal)
-        self.num_parts = mla.default_num_parts(self.s_q, self.h_q, fp8=self.fp8)
+        self.num_parts = mla.default_num_parts(self.s_q, self.h_q)
         dev = self.q.device
         self.meta = torch.empty((self.num_parts, mla.META_INTS), dtype=torch.int32, device=dev)
         self.split_base = torch.empty((self.batch + 1,), dtype=torch.int32, device=dev)
@@ -236,10 +236,8 @@ def roofline(rep, workload):
     rows = cfg["s_q"] * cfg["h_q"]
     if rows < 64:
         kernel = "decode_rowgroup_kernel<%s>" % ("true" if cfg["fp8"] else "false")
-    elif cfg["fp8"]:
-        kernel = "decode_rows64_fp8_kernel"
     else:
-        kernel = "decode_rows128_kernel" if rows % 128 == 0 else "decode_rows64_kernel"
+        kernel = "decode_rows64_fp8_kernel" if cfg["fp8"] else "decode_rows64_kernel"
     traffic = measured_traffic(kernel, workload)
     if rep["bound"] == "hbm":
         achieved, peak, unit = rep["attn_gbs"], PEAK_HBM_GBS, "GB/s"

@@ -85,11 +85,9 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
  * 1 + (s_q * h_q) / 64. */
 int mla_plan_overhead(int s_q, int h_q);
 
-/* Plan size suited to the kernel that runs these sizes on `device` (a multiple
- * of 8 derived from the CU count and the rows per work-group of that kernel,
- * which depends on the cache format: kv_format 0 = bf16, 1 = FP8); < 0 on
- * error (status code).  Needs a visible GPU. */
-int mla_default_num_parts(int device, int s_q, int h_q, int kv_format);
+/* Plan size suited to the kernels on `device` (a multiple of 8 derived from
+ * the CU count); < 0 on error (status code).  Needs a visible GPU. */
+int mla_default_num_parts(int device, int s_q, int h_q);
 
 /*
  * Split-KV plan.  Cuts the batch's pages into num_parts contiguous pieces of

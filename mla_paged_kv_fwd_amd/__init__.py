@@ -37,7 +37,7 @@ _SIGNATURES = {
     "mla_metadata_ints": (_SZ, [_I]),
     "mla_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "mla_plan_overhead": (_I, [_I, _I]),
-    "mla_default_num_parts": (_I, [_I, _I, _I, _I]),
+    "mla_default_num_parts": (_I, [_I, _I, _I]),
     "mla_get_metadata": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "mla_get_metadata_host": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "mla_decode_fwd": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
@@ -94,24 +94,23 @@ def workspace_bytes(batch, s_q, h_q, num_parts):
     return lib().mla_workspace_bytes(batch, s_q, h_q, num_parts)
 
 
-def default_num_parts(s_q, h_q, device=None, fp8=False):
+def default_num_parts(s_q, h_q, device=None):
     dev = torch.cuda.current_device() if device is None else int(device)
-    n = lib().mla_default_num_parts(dev, s_q, h_q, 1 if fp8 else 0)
+    n = lib().mla_default_num_parts(dev, s_q, h_q)
     if n < 0:
         _check(n, "mla_default_num_parts")
     return n
 
 
-def get_metadata(seqlens, s_q, h_q, num_parts=None, fp8=False):
+def get_metadata(seqlens, s_q, h_q, num_parts=None):
     """Plan split-KV work on the GPU.  seqlens: int32 CUDA tensor [batch].
-    Without num_parts, the plan size suits the kernel for the cache format.
 
     Returns (meta int32 [num_parts, 8], split_base int32 [batch + 1], num_parts).
     """
     if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
         raise MlaError("seqlens must be a contiguous int32 CUDA tensor")
     if num_parts is None:
-        num_parts = default_num_parts(s_q, h_q, seqlens.device.index, fp8)
+        num_parts = default_num_parts(s_q, h_q, seqlens.device.index)
     batch = seqlens.shape[0]
     meta = torch.empty((num_parts, META_INTS), dtype=torch.int32, device=seqlens.device)
     split_base = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
@@ -195,7 +194,7 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
     _validate(q, kcache, block_table, seqlens, fp8)
     b, s_q, h_q, _ = q.shape
     if meta is None:
-        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts, fp8)
+        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts)
     out, lse = _outputs(q, out, lse)
     workspace = _workspace(q, num_parts, workspace)
     fn = lib().mla_decode_fwd_fp8 if fp8 else lib().mla_decode_fwd

@@ -13,7 +13,6 @@ void plan_host(const int32_t *seqlens, int batch, int c, int num_parts, int32_t 
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 int decode_rows_per_group();
 hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream);
-hipError_t launch_decode_rows128(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
@@ -25,15 +24,9 @@ static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::k
 
 namespace {
 
-// Kernel choice by query rows per request M: 128 rows per work-group (every
-// wave owns 32 rows) for bf16 caches when M is a multiple of 128; 64 rows per
-// work-group with specialised score / value waves for the other M >= 64 and
-// for FP8 caches; 16 rows per work-group otherwise.
-bool use_rows128(int M, int kv_format) { return kv_format == 0 && M % 128 == 0; }
+// Kernel choice: 64 query rows per work-group with specialised score / value
+// waves when a request has at least 64 rows; 16 rows per work-group otherwise.
 bool use_rows64(int M) { return M >= 64; }
-int rows_per_group(int M, int kv_format) {
-    return use_rows128(M, kv_format) ? 128 : use_rows64(M) ? 64 : 0;
-}
 
 bool shape_supported(int s_q, int h_q) {
     return (s_q == 1 || s_q == 2) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
@@ -92,10 +85,7 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
     hipError_t e;
-    if (use_rows128(M, kv_format)) {
-        a.row_groups = M / 128;
-        e = mla::launch_decode_rows128(a, (hipStream_t)stream);
-    } else if (use_rows64(M)) {
+    if (use_rows64(M)) {
         a.row_groups = M / 64;
         e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
                            : mla::launch_decode_rows64(a, (hipStream_t)stream);
@@ -151,9 +141,9 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
 
 int mla_plan_overhead(int s_q, int h_q) { return mla::plan_overhead(s_q, h_q); }
 
-int mla_default_num_parts(int device, int s_q, int h_q, int kv_format) {
+int mla_default_num_parts(int device, int s_q, int h_q) {
     if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
-    if (device < 0 || device >= 64 || (kv_format != 0 && kv_format != 1)) return MLA_ERR_INVALID_ARG;
+    if (device < 0 || device >= 64) return MLA_ERR_INVALID_ARG;
     if (g_cu_count[device] <= 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
@@ -161,13 +151,11 @@ int mla_default_num_parts(int device, int s_q, int h_q, int kv_format) {
             return MLA_ERR_HIP;
         g_cu_count[device] = cus;
     }
-    // one work-group per CU: a part spans M / 128 or M / 64 work-groups in the
-    // 128- and 64-row kernels and M / 16 (run in several rounds) in the 16-row
-    // kernel
+    // one work-group per CU: a part spans M / 64 work-groups in the 64-row
+    // kernel and M / 16 (run in several rounds) in the 16-row kernel
     const int M = s_q * h_q;
     int parts = g_cu_count[device];
-    const int rows = rows_per_group(M, kv_format);
-    if (rows > 0) parts = parts / (M / rows);
+    if (use_rows64(M)) parts = parts / (M / 64);
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
 }

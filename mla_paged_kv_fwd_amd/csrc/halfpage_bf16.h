@@ -1,6 +1,6 @@
-// LDS layout of one 32-token half-page of a bf16 cache, shared by the 64-row
-// and 128-row bf16 decode kernels, with the lane addressing of its
-// direct-to-LDS loads and of the MFMA operand reads.
+// LDS layout of one 32-token half-page of a bf16 cache as the 64-row bf16
+// decode kernel holds it, with the lane addressing of its direct-to-LDS loads
+// and of the MFMA operand reads.
 //
 // A half-page is 36 KB: 2304 slots of 16 bytes.  Token tau (0..31), 16-byte
 // chunk c (0..71) of its 1152-byte row sits in slot

@@ -55,7 +55,7 @@ def test_shapes_with_poisoned_tails_match_oracle(seqlens, s_q, h_q, causal, fp8)
 GROWING = [
     # seqlens, s_q, h_q, causal, num_parts, fp8: RoPE keys scaled up along the
     # sequence, so each row's running max keeps rising (the 16-row kernel
-    # rescales, the 64- and 128-row kernels restart segments)
+    # rescales, the 64-row kernels restart segments)
     ([300, 1000, 2100], 1, 128, False, 8, False),
     ([1000, 3000], 2, 64, True, 4, False),
     ([1000, 3000], 1, 64, False, 4, False),
@@ -111,7 +111,7 @@ def test_result_does_not_depend_on_the_split(num_parts):
 
 
 @pytest.mark.parametrize("num_parts", [1, 7, 64, 256])
-def test_result_does_not_depend_on_the_split_128_rows(num_parts):
+def test_result_does_not_depend_on_the_split_256_rows(num_parts):
     case = W.make_case([900, 33, 2000, 64], 2, 128, seed=17, causal=True, spare_pages=2,
                        poison=True)
     out, lse = run_gpu(case, num_parts=num_parts)
