@@ -5,7 +5,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 package never imports the library: the two share no code.
 
 ``mla_oracle.c`` holds the attention definition (fp64), the OCP E4M3FN decode
-and the LSE merge; ``plan.py`` holds the split-KV plan definition.  Every
+and encode, the FP8 record writer (the cache writer's definition) and the LSE
+merge; ``plan.py`` holds the split-KV plan definition.  Every
 function here is a thin ctypes wrapper or a plain loop.
 """
 import ctypes
@@ -54,6 +55,13 @@ def _load():
     lib.mla_oracle_fp8_record_values.argtypes = [P, P]
     lib.mla_oracle_fp8_record_values.restype = None
     lib.mla_oracle_fp8_record_bytes.restype = ctypes.c_int
+    lib.mla_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.mla_oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.mla_oracle_fp8_record_from_row.argtypes = [P, P]
+    lib.mla_oracle_fp8_record_from_row.restype = None
+    lib.mla_oracle_kv_write.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P,
+                                        ctypes.c_int, P]
+    lib.mla_oracle_kv_write.restype = None
     lib.mla_oracle_bf16_token_bytes.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -137,3 +145,32 @@ def fp8_record_bytes():
 
 def bf16_token_bytes():
     return _load().mla_oracle_bf16_token_bytes()
+
+
+def e4m3_encode(x):
+    """OCP E4M3FN code of a finite fp32 value with |x| <= 448 (nearest, ties
+    to the even code)."""
+    return int(_load().mla_oracle_e4m3_encode(ctypes.c_float(float(x))))
+
+
+def fp8_record_from_row(row):
+    """One bf16 row (uint16 bits [576]) -> its 656-byte FP8 record."""
+    row = np.ascontiguousarray(row, dtype=np.uint16).reshape(D_QK)
+    rec = np.zeros(656, dtype=np.uint8)
+    _load().mla_oracle_fp8_record_from_row(_ptr(row), _ptr(rec))
+    return rec
+
+
+def kv_write(k_new, block_table, seqlens, cache, kind):
+    """Cache writer: returns a copy of `cache` with the rows of k_new (uint16
+    bf16 bits [batch, n_new, 576]) written at the end of each request (kind 0:
+    bf16 rows, cache uint16 [pages, 64, 576]; kind 1: FP8 records, cache uint8
+    [pages, 64, 656])."""
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    batch, n_new = k_new.shape[0], k_new.shape[1]
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    out = np.array(cache, copy=True)
+    _load().mla_oracle_kv_write(_ptr(k_new), batch, n_new, _ptr(bt), bt.shape[1], _ptr(sl),
+                                int(kind), _ptr(out))
+    return out

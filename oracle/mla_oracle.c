@@ -28,6 +28,11 @@
  *     RoPE slice kept in BF16): a token record is 512 OCP E4M3FN codes, then
  *     four little-endian fp32 scales (one per 128-dim tile), then 64 bf16
  *     RoPE values.  Dequantised key = e4m3(code) * scale[d / 128].
+ *   - Writing that record from a bf16 row (the cache writer): the pages give
+ *     the record but not the quantiser; the plain reading used here maps each
+ *     tile's absolute maximum to E4M3's largest finite value, 448:
+ *     scale = amax / 448 (fp32), code = E4M3 nearest-even of clip(x / scale,
+ *     +-448) (fp32 division), and an all-zero tile gets scale 0 and codes 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -64,6 +69,80 @@ double mla_oracle_e4m3_value(uint8_t code)
     else
         mag = ldexp(1.0 + (double)m / 8.0, e - 7);
     return sign ? -mag : mag;
+}
+
+/*
+ * OCP E4M3FN encoding of a finite fp32 value with |x| <= 448: the nearest
+ * representable value, ties to the even code (last mantissa bit 0).  Plain
+ * search over the 127 non-negative finite codes, whose values increase with
+ * the code; the sign bit is copied (so -0 encodes as 0x80).
+ */
+uint8_t mla_oracle_e4m3_encode(float x)
+{
+    double a = fabs((double)x), best_d = INFINITY;
+    int c, best = 0;
+    for (c = 0; c < 127; ++c) {
+        double d = fabs(mla_oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+/* One 576-dim bf16 row -> one 656-byte FP8 record (see the header). */
+void mla_oracle_fp8_record_from_row(const uint16_t *row, uint8_t *rec)
+{
+    int t, d;
+    for (t = 0; t < ORC_D_V / 128; ++t) {
+        float amax = 0.f, scale;
+        for (d = 128 * t; d < 128 * (t + 1); ++d) {
+            float v = fabsf((float)orc_bf16(row[d]));
+            if (v > amax) amax = v;
+        }
+        scale = amax / 448.0f;
+        memcpy(rec + ORC_FP8_SCALES_AT + 4 * t, &scale, 4);
+        for (d = 128 * t; d < 128 * (t + 1); ++d) {
+            float x;
+            if (!(scale > 0.f)) {
+                rec[d] = 0;
+                continue;
+            }
+            x = (float)orc_bf16(row[d]) / scale;
+            if (x > 448.0f) x = 448.0f;
+            if (x < -448.0f) x = -448.0f;
+            rec[d] = mla_oracle_e4m3_encode(x);
+        }
+    }
+    memcpy(rec + ORC_FP8_ROPE_AT, row + ORC_D_V, 2 * (ORC_D_QK - ORC_D_V));
+}
+
+/*
+ * Cache writer.  k_new bf16 [batch][n_new][576]: row i of request b is the
+ * token at position L_b - n_new + i of that request (seqlens already count
+ * the new rows); rows at negative positions are skipped.  The token's page is
+ * block_table[b][pos / 64], its slot pos % 64.  kind 0 copies the bf16 row
+ * into a [pages][64][576] cache; kind 1 writes the FP8 record into a
+ * [pages][64][656] cache.  Nothing else in the cache changes.
+ */
+void mla_oracle_kv_write(const uint16_t *k_new, int batch, int n_new, const int32_t *block_table,
+                         int64_t bt_stride, const int32_t *seqlens, int kind, void *cache)
+{
+    int b, i;
+    for (b = 0; b < batch; ++b)
+        for (i = 0; i < n_new; ++i) {
+            int64_t pos = (int64_t)seqlens[b] - n_new + i, phys;
+            const uint16_t *row = k_new + ((int64_t)b * n_new + i) * ORC_D_QK;
+            if (pos < 0) continue;
+            phys = block_table[(int64_t)b * bt_stride + pos / ORC_PAGE];
+            if (kind == 0)
+                memcpy((uint16_t *)cache + (phys * ORC_PAGE + pos % ORC_PAGE) * ORC_D_QK, row,
+                       2 * ORC_D_QK);
+            else
+                mla_oracle_fp8_record_from_row(
+                    row, (uint8_t *)cache + (phys * ORC_PAGE + pos % ORC_PAGE) * ORC_FP8_RECORD);
+        }
 }
 
 /* One cached token's 576-dim key, widened to double. */
