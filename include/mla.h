@@ -173,6 +173,36 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
                               int num_parts, const void *workspace, size_t workspace_bytes,
                               void *out, float *lse, void *stream);
 
+/*
+ * Cache writer: stores the rows of the newest n_new tokens of every request
+ * in the paged cache.  Row i of request b (k_new[b][i]: 576 bf16 values, 512
+ * latent then 64 RoPE) is the token at position L_b - n_new + i (seqlens count
+ * the new tokens, as for decode; rows at negative positions are skipped): page
+ * block_table[b * block_table_stride + pos / 64], slot pos % 64.
+ *   k_new       bf16 [batch][n_new][576] (device)
+ *   kcache      mla_kv_cache_write: bf16 [num_pages][64][576], the row is
+ *               copied.  mla_kv_cache_write_fp8: [num_pages][64][656] records
+ *               (layout above); per 128-dim latent tile scale = amax / 448 in
+ *               fp32 (448 is E4M3FN's largest finite value; an all-zero tile
+ *               gets scale 0 and zero codes) and code = E4M3FN
+ *               round-to-nearest-even of x / scale (fp32 division, clipped to
+ *               +-448); the RoPE dims are copied.  The pages give the record
+ *               layout (DeepSeek KB page, "Key Contributions") but not the
+ *               quantiser; this is its plain reading.
+ *   n_new >= 1; batch * n_new < 2^31.  A decode step appends s_q rows per
+ *   request; a prefill passes whole sequences right-aligned in n_new rows.
+ * Nothing else in the cache is written.  One kernel on `stream`; rows of
+ * different requests must not map to the same slot.
+ */
+mla_status mla_kv_cache_write(const void *k_new, int batch, int n_new,
+                              const int32_t *block_table, int block_table_stride,
+                              const int32_t *seqlens, void *kcache, int64_t num_pages,
+                              void *stream);
+mla_status mla_kv_cache_write_fp8(const void *k_new, int batch, int n_new,
+                                  const int32_t *block_table, int block_table_stride,
+                                  const int32_t *seqlens, void *kcache_fp8, int64_t num_pages,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

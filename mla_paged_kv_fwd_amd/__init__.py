@@ -13,7 +13,8 @@ import torch
 __all__ = [
     "MlaError", "lib", "D_QK", "D_V", "PAGE", "FP8_RECORD", "META_INTS",
     "default_num_parts", "plan_overhead", "workspace_bytes", "get_metadata",
-    "get_metadata_host", "decode", "decode_attn", "decode_combine", "status_string",
+    "get_metadata_host", "decode", "decode_attn", "decode_combine", "kv_cache_write",
+    "status_string",
 ]
 
 D_QK = 576
@@ -47,6 +48,8 @@ _SIGNATURES = {
     "mla_decode_attn": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P,
                              _SZ, _P, _P, _P]),
     "mla_decode_combine": (_I, [_P, _I, _I, _I, _I, _P, _SZ, _P, _P, _P]),
+    "mla_kv_cache_write": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
+    "mla_kv_cache_write_fp8": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
 }
 
 
@@ -203,3 +206,28 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
               _ptr(split_base), num_parts, _ptr(workspace), workspace.numel(), _ptr(out),
               _ptr(lse), _stream()), "mla_decode_fwd")
     return out, lse
+
+
+def kv_cache_write(k_new, block_table, seqlens, kcache, fp8=False):
+    """Store k_new (bf16 [batch, n_new, 576]) as the newest n_new tokens of
+    every request: bf16 rows into a bf16 cache, or 656-byte FP8 records into
+    a uint8 [pages, 64, 656] cache.  Writes kcache in place and returns it."""
+    if k_new.dtype != torch.bfloat16 or k_new.dim() != 3 or k_new.shape[-1] != D_QK:
+        raise MlaError("k_new must be bf16 [batch, n_new, 576]")
+    if fp8:
+        if kcache.dtype != torch.uint8 or tuple(kcache.shape[1:]) != (PAGE, FP8_RECORD):
+            raise MlaError("fp8 kcache must be uint8 [pages, 64, 656]")
+    elif kcache.dtype != torch.bfloat16 or tuple(kcache.shape[1:]) != (PAGE, D_QK):
+        raise MlaError("kcache must be bf16 [pages, 64, 576]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise MlaError("block_table must be int32 [batch, width]")
+    if seqlens.dtype != torch.int32 or seqlens.dim() != 1:
+        raise MlaError("seqlens must be int32 [batch]")
+    for t in (k_new, kcache, block_table, seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise MlaError("all tensors must be contiguous CUDA tensors")
+    batch, n_new = k_new.shape[0], k_new.shape[1]
+    fn = lib().mla_kv_cache_write_fp8 if fp8 else lib().mla_kv_cache_write
+    _check(fn(_ptr(k_new), batch, n_new, _ptr(block_table), block_table.shape[1], _ptr(seqlens),
+              _ptr(kcache), kcache.shape[0], _stream()), "mla_kv_cache_write")
+    return kcache

@@ -14,6 +14,9 @@ hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 int decode_rows_per_group();
 hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const int32_t *block_table,
+                           int64_t bt_stride, const int32_t *seqlens, void *cache, bool fp8,
+                           hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -110,6 +113,19 @@ mla_status combine_impl(const int32_t *split_base, int batch, int s_q, int h_q, 
     const float *lse_part = o_part + slots * M * mla::kDV;
     hipError_t e = mla::launch_combine(split_base, batch, M, o_part, lse_part, (uint16_t *)out,
                                        lse, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status kv_write_impl(const void *k_new, int batch, int n_new, const int32_t *block_table,
+                         int block_table_stride, const int32_t *seqlens, void *kcache,
+                         int64_t num_pages, bool fp8, void *stream) {
+    if (!k_new || !block_table || !seqlens || !kcache) return MLA_ERR_INVALID_ARG;
+    if (batch <= 0 || n_new <= 0 || block_table_stride < 1 || num_pages <= 0)
+        return MLA_ERR_INVALID_ARG;
+    if (batch > mla::kMaxBatch || (int64_t)batch * n_new > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+    hipError_t e = mla::launch_kv_write((const uint16_t *)k_new, batch, n_new, block_table,
+                                        block_table_stride, seqlens, kcache, fp8,
+                                        (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -233,6 +249,22 @@ mla_status mla_decode_fwd_fp8(const void *q, const void *kcache_fp8, int64_t num
     return decode_fwd(q, kcache_fp8, 1, num_pages, block_table, block_table_stride, seqlens, batch,
                       s_q, h_q, softmax_scale, causal, meta, split_base, num_parts, workspace,
                       workspace_bytes_, out, lse, stream);
+}
+
+mla_status mla_kv_cache_write(const void *k_new, int batch, int n_new,
+                              const int32_t *block_table, int block_table_stride,
+                              const int32_t *seqlens, void *kcache, int64_t num_pages,
+                              void *stream) {
+    return kv_write_impl(k_new, batch, n_new, block_table, block_table_stride, seqlens, kcache,
+                         num_pages, false, stream);
+}
+
+mla_status mla_kv_cache_write_fp8(const void *k_new, int batch, int n_new,
+                                  const int32_t *block_table, int block_table_stride,
+                                  const int32_t *seqlens, void *kcache_fp8, int64_t num_pages,
+                                  void *stream) {
+    return kv_write_impl(k_new, batch, n_new, block_table, block_table_stride, seqlens,
+                         kcache_fp8, num_pages, true, stream);
 }
 
 }  // extern "C"

@@ -79,10 +79,17 @@ double mla_oracle_e4m3_value(uint8_t code)
  */
 uint8_t mla_oracle_e4m3_encode(float x)
 {
+    static double value[127];
+    static int have_values = 0;
     double a = fabs((double)x), best_d = INFINITY;
     int c, best = 0;
+    if (!have_values) {  /* the code table, from the decoding definition */
+        for (c = 0; c < 127; ++c)
+            value[c] = mla_oracle_e4m3_value((uint8_t)c);
+        have_values = 1;
+    }
     for (c = 0; c < 127; ++c) {
-        double d = fabs(mla_oracle_e4m3_value((uint8_t)c) - a);
+        double d = fabs(value[c] - a);
         if (d < best_d || (d == best_d && (c & 1) == 0)) {
             best_d = d;
             best = c;

@@ -105,6 +105,22 @@ def test_metadata_argument_errors():
     assert fn(FAKE, 2, 1, 16, 100000, FAKE, FAKE, None) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("name", ["mla_kv_cache_write", "mla_kv_cache_write_fp8"])
+def test_cache_writer_argument_errors(name):
+    lib = load_lib()
+    fn = getattr(lib, name)
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert fn(None, 2, 1, FAKE, 4, FAKE, FAKE, 10, None) == INVALID      # null k_new
+    assert fn(FAKE, 2, 1, FAKE, 4, None, FAKE, 10, None) == INVALID      # null seqlens
+    assert fn(FAKE, 2, 1, FAKE, 4, FAKE, None, 10, None) == INVALID      # null cache
+    assert fn(FAKE, 0, 1, FAKE, 4, FAKE, FAKE, 10, None) == INVALID      # batch 0
+    assert fn(FAKE, 2, 0, FAKE, 4, FAKE, FAKE, 10, None) == INVALID      # n_new 0
+    assert fn(FAKE, 2, 1, FAKE, 0, FAKE, FAKE, 10, None) == INVALID      # stride 0
+    assert fn(FAKE, 2, 1, FAKE, 4, FAKE, FAKE, 0, None) == INVALID       # no pages
+    assert fn(FAKE, 16384, 1 << 17, FAKE, 4, FAKE, FAKE, 10, None) == UNSUPPORTED  # >= 2^31 rows
+
+
 def _host_plan(lib, seqlens, s_q, h_q, parts):
     sl = np.ascontiguousarray(seqlens, dtype=np.int32)
     meta = np.full((parts, 8), 12345, dtype=np.int32)
