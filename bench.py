@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
-    p.add_argument("--extra", default="computebound,fp8,longctx",
+    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite",
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -158,6 +158,52 @@ class Runner:
             roofline_frac=round(max(gbs / PEAK_HBM_GBS, tfl / PEAK_BF16_TFLOPS), 4))
 
 
+def kv_write_bench(steps, warmup):
+    """The cache writer on the FP8 workload's cache written whole, as a prefill
+    would: 64 requests x 16384 rows of 576 bf16 values quantised into 656-byte
+    records (the kernel reads 1152 B and writes 656 B per row).  Also the
+    decode append of the same batch (2 rows per request).  Launches timed back
+    to back between two events on the launch stream."""
+    import torch
+    import mla_paged_kv_fwd_amd as mla
+    import workloads as W
+
+    batch, length = 64, 16384
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    pages = length // W.PAGE
+    perm = torch.randperm(batch * pages, generator=g, device="cuda").to(torch.int32)
+    bt = perm.reshape(batch, pages).contiguous()
+    sl = torch.full((batch,), length, dtype=torch.int32, device="cuda")
+    kc = torch.zeros((batch * pages, W.PAGE, W.FP8_RECORD), dtype=torch.uint8, device="cuda")
+    k_new = torch.randn((batch, length, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    lib = mla.lib()
+
+    def timed(rows):
+        src = k_new if rows == length else k_new[:, length - rows:].contiguous()  # kept alive
+        args = (src.data_ptr(), batch, rows, bt.data_ptr(), pages, sl.data_ptr(), kc.data_ptr(),
+                kc.shape[0], stream.cuda_stream)
+        for _ in range(warmup):
+            lib.mla_kv_cache_write_fp8(*args)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(steps):
+            if lib.mla_kv_cache_write_fp8(*args) != 0:
+                raise RuntimeError("mla_kv_cache_write_fp8 failed")
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / steps * 1e3
+
+    us = timed(length)
+    rows = batch * length
+    alg = rows * (2 * W.D_QK + W.FP8_RECORD) + batch * pages * 4 + batch * 4
+    us_append = timed(2)
+    return dict(kernel="kv_write_kernel<true>", rows=rows, us=round(us, 2), alg_bytes=alg,
+                gbs=round(alg / us / 1e3, 1), hbm_frac=round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
+                bound="hbm", append_rows=2 * batch, append_us=round(us_append, 2))
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     rocprofv3 counter summary under profiles/, if the kernel's source still
@@ -275,6 +321,12 @@ def main():
     workloads = {args.workload: rep}
     del main_r
     for name in [x for x in args.extra.split(",") if x]:
+        if name == "kvwrite":
+            rep_x = kv_write_bench(args.steps, args.warmup)
+            print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
+            workloads[name] = rep_x
+            torch.cuda.empty_cache()
+            continue
         r = Runner(name)
         rep_x = r.report(r.measure(args.steps, args.warmup))
         print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)

@@ -20,11 +20,13 @@ def _lib():
 
 
 def _rows(rng, batch, n_new):
-    """bf16 rows with per-tile magnitudes from 2^-24 to 2^12, zero tiles,
-    signed zeros and values that land on E4M3 subnormals after scaling."""
+    """bf16 rows with per-tile magnitudes from 2^-24 to 2^12, tiles near
+    2^-70 (below the writer's fast-division range), zero tiles, signed zeros
+    and values that land on E4M3 subnormals after scaling."""
     x = rng.normal(0, 1, (batch, n_new, 576)).astype(np.float32)
     tiles = x[..., :512].reshape(batch, n_new, 4, 128)
     tiles *= np.exp2(rng.integers(-24, 13, size=(batch, n_new, 4, 1))).astype(np.float32)
+    tiles[rng.random(tiles.shape[:3]) < 0.05] *= np.float32(2.0 ** -70)
     small = rng.random(tiles.shape) < 0.05
     tiles[small] *= np.float32(2.0 ** -14)          # subnormal codes
     tiles[rng.random(tiles.shape[:3]) < 0.05] = 0.0  # whole zero tiles
