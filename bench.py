@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
-    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite",
+    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,fp8_accuracy",
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -204,6 +204,49 @@ def kv_write_bench(steps, warmup):
                 bound="hbm", append_rows=2 * batch, append_us=round(us_append, 2))
 
 
+def fp8_accuracy():
+    """FP8 cache against bf16 cache on the same latent: the FP8 workload's
+    shape (64 requests x 16384 tokens, s_q 1, h_q 128), N(0,1) rows rounded to
+    bf16, written once as bf16 rows and once as FP8 records by the cache
+    writer; both decoded with the same queries.  Reports how far the FP8
+    result moves from the bf16 one (a property of the format and its
+    quantiser, not a parity check)."""
+    import math
+
+    import torch
+    import mla_paged_kv_fwd_amd as mla
+    import workloads as W
+
+    batch, length, h_q = 64, 16384, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78)
+    pages = length // W.PAGE
+    bt = torch.randperm(batch * pages, generator=g, device="cuda").to(torch.int32).reshape(
+        batch, pages).contiguous()
+    sl = torch.full((batch,), length, dtype=torch.int32, device="cuda")
+    rows = torch.randn((batch, length, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((batch, 1, h_q, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
+    kc16 = torch.empty((batch * pages, W.PAGE, W.D_QK), dtype=torch.bfloat16, device="cuda")
+    kc8 = torch.empty((batch * pages, W.PAGE, W.FP8_RECORD), dtype=torch.uint8, device="cuda")
+    mla.kv_cache_write(rows, bt, sl, kc16)
+    mla.kv_cache_write(rows, bt, sl, kc8, fp8=True)
+    del rows
+    scale = 1.0 / math.sqrt(W.D_QK)
+    o16, l16 = mla.decode(q, kc16, bt, sl, scale, False)
+    o8, l8 = mla.decode(q, kc8, bt, sl, scale, False, fp8=True)
+    torch.cuda.synchronize()
+    d = o8.float() - o16.float()
+    rel = (d.norm() / o16.float().norm()).item()
+    res = dict(shape=f"batch {batch} x {length}, s_q 1, h_q {h_q}",
+               out_max_abs=round(d.abs().max().item(), 6), out_rel_l2=round(rel, 6),
+               out_ref_max_abs=round(o16.float().abs().max().item(), 6),
+               lse_max_abs=round((l8 - l16).abs().max().item(), 6),
+               lse_mean_abs=round((l8 - l16).abs().mean().item(), 6))
+    del kc16, kc8
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     rocprofv3 counter summary under profiles/, if the kernel's source still
@@ -321,8 +364,8 @@ def main():
     workloads = {args.workload: rep}
     del main_r
     for name in [x for x in args.extra.split(",") if x]:
-        if name == "kvwrite":
-            rep_x = kv_write_bench(args.steps, args.warmup)
+        if name in ("kvwrite", "fp8_accuracy"):
+            rep_x = kv_write_bench(args.steps, args.warmup) if name == "kvwrite" else fp8_accuracy()
             print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
             workloads[name] = rep_x
             torch.cuda.empty_cache()
