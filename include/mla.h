@@ -38,7 +38,7 @@
  *       out   bf16  [batch][s_q][h_q][512]
  *       lse   fp32  [batch][s_q][h_q]      (natural log)
  *       seqlens int32 [batch]; block_table int32 [batch][block_table_stride]
- *   - Shapes supported: s_q in {1, 2}; h_q in {16, 32, 64, 128}; one shared
+ *   - Shapes supported: s_q in {1, 2, 4}; h_q in {16, 32, 64, 128}; one shared
  *     KV head; d_qk 576, d_v 512, page 64.  Others: MLA_ERR_UNSUPPORTED.
  *   - Argument errors that the host can see are reported before any HIP call.
  *     Device-resident contents (page ids inside [0, num_pages), lengths that

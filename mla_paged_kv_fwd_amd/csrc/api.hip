@@ -32,7 +32,7 @@ namespace {
 bool use_rows64(int M) { return M >= 64; }
 
 bool shape_supported(int s_q, int h_q) {
-    return (s_q == 1 || s_q == 2) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
+    return (s_q == 1 || s_q == 2 || s_q == 4) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
 }
 
 mla_status check_plan_args(int batch, int s_q, int h_q, int num_parts) {

@@ -111,10 +111,14 @@ __device__ __forceinline__ void dequant_slice(const lds_u8 *f8, lds_u8 *bf, int 
 
 constexpr float kRescaleLog2 = 8.f;
 
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
 struct RowState {
     f32x4 o[kDV / 16];  // O^T tiles: lane holds dims 16*dt + 4*(lane/16) + i of row lane%16
     float m;            // running max of scaled scores (log2 domain)
-    float lsum;         // this lane's share of the running sum
+    float lsum;         // this lane's share of the running sum (for the lse)
+    float wsum;         // the same sum over the weights as the value product used
+                        // them (bf16-rounded for a bf16 cache); normalises the output
 };
 
 // Scores, online softmax and PV for one 16-token slice held in LDS (bf16,
@@ -196,6 +200,15 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
         for (int i = 0; i < 4; ++i)
             pf[t][i] = (short)f32_to_bf16_bits(FP8 ? p[i] * tsc[i][t] : p[i]);
     }
+    // the output's normaliser: the weights as the value product uses them
+    // (FP8: each 128-dim value tile has its own scaled copy of P, so no single
+    // rounded sum matches them and the fp32 sum is used)
+    if constexpr (FP8) {
+        st.wsum = st.wsum * alpha + psum;
+    } else {
+        const auto pw = __builtin_bit_cast(u32x2_t, pf[0]);
+        st.wsum = st.wsum * alpha + add_bf16_pair(pw[1], add_bf16_pair(pw[0], 0.f));
+    }
     // O^T (512 dims x 16 rows) += V^T (512 x 16 tokens) . P^T (16 tokens x 16 rows)
     const int vp = (lr >> 1) & 1;  // chunk parity of this lane's V reads
     const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ vp) + (lr >> 2)) * 16 + 8 * (lr & 1);
@@ -215,6 +228,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
     // The read-only tables arrive as separate restrict-qualified arguments so
     // that their uniform reads compile to scalar loads.
     constexpr int kWaveLds = FP8 ? (2 * kSliceFp8 + kSliceBf16) : (2 * kSliceBf16);
+    static_assert(4 * (kWaves * kRows * kXStride + 3 * kWaves * kRows) <= kWaves * kWaveLds,
+                  "the merge buffers fit in the slice buffers");
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWaves * kWaveLds];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
@@ -270,6 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
         for (int dt = 0; dt < kDV / 16; ++dt) st.o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
         st.m = -INFINITY;
         st.lsum = 0.f;
+        st.wsum = 0.f;
 
         int phys_ahead = (j0 < j1) ? bt[j0 + 1] : 0;
         for (int j = j0; j <= j1; ++j) {
@@ -292,16 +308,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
 
         // ---- merge the 4 waves' states and write the result
         st.lsum = wave_sum16(st.lsum);
+        st.wsum = wave_sum16(st.wsum);
         __syncthreads();  // every wave is done reading its slices
         float *X = (float *)smem_raw;                 // [4][16][kXStride]
         float *Mw = X + kWaves * kRows * kXStride;     // [4][16]
         float *Lw = Mw + kWaves * kRows;               // [4][16]
+        float *Rw = Lw + kWaves * kRows;               // [4][16]
 #pragma unroll
         for (int dt = 0; dt < kDV / 16; ++dt)
             *(f32x4 *)(X + (w * kRows + lr) * kXStride + 16 * dt + 4 * lg) = st.o[dt];
         if (lg == 0) {
             Mw[w * kRows + lr] = st.m;
             Lw[w * kRows + lr] = st.lsum;
+            Rw[w * kRows + lr] = st.wsum;
         }
         __syncthreads();
         {
@@ -312,13 +331,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
                 mw[v] = Mw[v * kRows + r];
                 mf = fmaxf(mf, mw[v]);
             }
-            float aw[kWaves], lf = 0.f;
+            float aw[kWaves], lf = 0.f, rf = 0.f;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) {
                 aw[v] = (mw[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[v] - mf);
                 lf += aw[v] * Lw[v * kRows + r];
+                rf += aw[v] * Rw[v * kRows + r];
             }
-            const float inv = lf > 0.f ? 1.f / lf : 0.f;
+            const float inv = rf > 0.f ? 1.f / rf : 0.f;
             const float lse_val = lf > 0.f ? (mf + log2f(lf)) * 0.69314718055994530942f : -INFINITY;
             const int orow = row0 + r;
             if (nsplit == 1) {

@@ -123,11 +123,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
             // kGrowLog2 (after scaling) makes the whole work-group restart the
             // segment with the larger reference (rows that have not seen a key
             // yet adopt their first max freely, their accumulators being zero).
-            float m_seen = -INFINITY, m, lsum;
+            // lsum: sum of the fp32 weights (for the lse); wsum: sum of the
+            // weights as rounded to bf16 for the value product, which
+            // normalises the output (the effective weights then sum to 1, so
+            // a row dominated by one key returns that key's value exactly)
+            float m_seen = -INFINITY, m, lsum, wsum;
             bool again;
             do {  // one pass over the segment; repeated only after a restart
                 m = m_seen;
                 lsum = 0.f;
+                wsum = 0.f;
                 again = false;
                 // Restart flags by step parity: in step t a score wave writes slot
                 // t % 2, and every wave reads slot (t + 1) % 2 (written in step
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     const bool overflow = mloc > m + grow;
                     flag_lds[2 * (t & 1) + w] = __builtin_amdgcn_ballot_w64(overflow) != 0;  // same value from every lane
                     const float mc = (m == -INFINITY) ? 0.f : m * c;
-                    float psum = 0.f;
+                    float psum = 0.f, rsum = 0.f;
                     unsigned pk[8];
 #pragma unroll
                     for (int i = 0; i < 16; i += 2) {
@@ -204,8 +209,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i + 1], c, -mc));
                         psum += p0 + p1;
                         pk[i >> 1] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+                        rsum = add_bf16_pair(pk[i >> 1], rsum);
                     }
                     lsum += psum;
+                    wsum += rsum;
                     // P^T operand blocks: (row tile w, k-step kk) -> 1 KB at P + (2 w + kk) KB
                     lds_u8 *P = smem + kPOff + (t & 1) * kPBytes;
                     *(u32x4 __attribute__((address_space(3))) *)(P + (2 * w + 0) * 1024 + lane * 16) =
@@ -219,8 +226,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 }
             } while (again);
             lsum += __shfl_xor(lsum, 32);
+            wsum += __shfl_xor(wsum, 32);
             if (h == 0) {
-                stat_lds[kRowsWG + 32 * w + l32] = lsum;
+                stat_lds[kRowsWG + 32 * w + l32] = wsum;
                 const float lse_val =
                     lsum > 0.f ? (m * c + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
                 if (sg.nsplit == 1)

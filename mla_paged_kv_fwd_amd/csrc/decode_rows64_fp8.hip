@@ -150,11 +150,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
             for (int ks = 0; ks < kDQk / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 #pragma unroll
             for (int ks = 0; ks < kDQk / 16; ++ks) asm volatile("" : : "v"(qf[ks]));
-            float m_seen = -INFINITY, m, lsum;
+            // lsum: sum of the fp32 weights (for the lse); wsum: sum of the
+            // weights as rounded to bf16 for the value product, which
+            // normalises the output
+            float m_seen = -INFINITY, m, lsum, wsum;
             bool again;
             do {  // one pass over the segment; repeated only after a restart
                 m = m_seen;
                 lsum = 0.f;
+                wsum = 0.f;
                 again = false;
                 bool ovf = false;
                 // Restart flags by step parity: in step t a score wave writes slot
@@ -264,13 +268,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     lsum += psum;
                     // P^T operand blocks: (row tile w, k-step kk) -> 1 KB at P + (2 w + kk) KB
                     lds_u8 *P = smem + kPOff + (t & 1) * kPBytes + (2 * w) * 1024 + lane * 16;
+                    float rsum = 0.f;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         const int i0 = 8 * kk;
-                        *(lds_u32x4 *)(P + kk * 1024) =
-                            (u32x4){pack_bf16(p[i0], p[i0 + 1]), pack_bf16(p[i0 + 2], p[i0 + 3]),
-                                    pack_bf16(p[i0 + 4], p[i0 + 5]), pack_bf16(p[i0 + 6], p[i0 + 7])};
+                        const u32x4 pw = {pack_bf16(p[i0], p[i0 + 1]), pack_bf16(p[i0 + 2], p[i0 + 3]),
+                                          pack_bf16(p[i0 + 4], p[i0 + 5]), pack_bf16(p[i0 + 6], p[i0 + 7])};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) rsum = add_bf16_pair(pw[e], rsum);
+                        *(lds_u32x4 *)(P + kk * 1024) = pw;
                     }
+                    wsum += rsum;
                 }
                 if (again) {
                     wait_vmcnt<0>();
@@ -278,8 +286,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                 }
             } while (again);
             lsum += __shfl_xor(lsum, 32);
+            wsum += __shfl_xor(wsum, 32);
             if (h == 0) {
-                stat_lds[kRowsWG + 32 * w + l32] = lsum;
+                stat_lds[kRowsWG + 32 * w + l32] = wsum;
                 const float lse_val =
                     lsum > 0.f ? (m * c + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
                 if (sg.nsplit == 1)

@@ -37,6 +37,13 @@ __device__ __forceinline__ float wave_sum16(float v) {
     return v;
 }
 
+// acc + the two bf16 values packed in w (one v_dot2c_f32_bf16 against 1, 1).
+__device__ __forceinline__ float add_bf16_pair(unsigned w, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(unsigned short, (__bf16)f);
 }

@@ -46,7 +46,7 @@ def test_sizes_and_overhead():
     assert lib.mla_metadata_ints(256) == 256 * 8
     assert lib.mla_workspace_bytes(128, 1, 16, 256) == (128 + 256) * 16 * 513 * 4
     assert lib.mla_workspace_bytes(0, 1, 16, 256) == 0
-    for s_q in (1, 2):
+    for s_q in (1, 2, 4):
         for h_q in (16, 32, 64, 128):
             assert lib.mla_plan_overhead(s_q, h_q) == oracle.plan_overhead(s_q, h_q)
 
@@ -85,6 +85,7 @@ def _decode(lib, **kw):
     (dict(h_q=8), UNSUPPORTED),
     (dict(h_q=48), UNSUPPORTED),
     (dict(s_q=3), UNSUPPORTED),
+    (dict(s_q=8), UNSUPPORTED),
     (dict(batch=100000), UNSUPPORTED),
     (dict(ws=None), WORKSPACE),
     (dict(ws_bytes=1000), WORKSPACE),

@@ -40,6 +40,11 @@ SHAPES = [
     ([5, 64, 257], 1, 128, False, True),
     ([1, 31, 32, 33, 63, 64, 65, 700], 1, 64, False, True),
     ([2, 66, 130, 400], 2, 128, True, True),
+    # four query tokens per request (multi-token prediction drafts)
+    ([3, 4, 5, 64, 131, 700], 4, 16, True, False),
+    ([3, 4, 5, 64, 131, 700], 4, 32, False, False),
+    ([4, 70, 300], 4, 128, True, False),
+    ([4, 70, 300], 4, 64, True, True),
 ]
 
 
@@ -64,6 +69,7 @@ GROWING = [
     ([300, 1000, 2100], 1, 128, False, 64, False),
     ([300, 1000, 2100], 1, 128, False, 8, True),
     ([1000, 3000], 2, 32, True, 4, True),
+    ([300, 1000, 2100], 4, 64, True, 8, False),
 ]
 
 

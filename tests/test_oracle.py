@@ -78,15 +78,20 @@ def test_noncausal_matches_torch_sdpa(seqlens, s_q, h_q):
             np.testing.assert_allclose(lse[b, i], rl, rtol=1e-12, atol=1e-12)
 
 
-def test_causal_rows_see_bottom_right_prefix():
-    # Query row i of s_q sees keys [0, L - (s_q - 1 - i)).
-    seqlens, s_q, h_q = [3, 64, 65, 130], 2, 4
+@pytest.mark.parametrize("s_q", [2, 4])
+def test_causal_rows_see_bottom_right_prefix(s_q):
+    # Query row i of s_q sees keys [0, L - (s_q - 1 - i)); with s_q = 4 and
+    # L = 3 the oldest row sees nothing
+    seqlens, h_q = [3, 64, 65, 130], 4
     case = W.make_case(seqlens, s_q, h_q, seed=12, permute=False, causal=True)
     out, lse = oracle.decode(case.q, case.cache, 0, case.block_table, case.seqlens, case.scale, True)
     for b in range(case.batch):
         keys = _contiguous_keys(case, b)
         for i in range(s_q):
             n = seqlens[b] - (s_q - 1 - i)
+            if n <= 0:
+                assert np.all(out[b, i] == 0) and np.all(np.isneginf(lse[b, i]))
+                continue
             ro, rl = _sdpa(_q_rows(case, b, i), keys[:n], case.scale)
             np.testing.assert_allclose(out[b, i], ro, rtol=1e-10, atol=1e-12)
             np.testing.assert_allclose(lse[b, i], rl, rtol=1e-12, atol=1e-12)
