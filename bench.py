@@ -36,6 +36,8 @@ def parse():
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--sweep", action="store_true",
+                   help="only run the shape sweep (one JSON line per shape)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 1 GiB device copies (to scale HBM counters)")
     return p.parse_args()
@@ -44,14 +46,16 @@ def parse():
 class Runner:
     """Device inputs, a preallocated plan / workspace / outputs, and a step."""
 
-    def __init__(self, name):
+    def __init__(self, name, inputs=None):
+        """`name`: a workload of workloads.CONFIGS, or a label when `inputs`
+        gives (q, kcache, block_table, seqlens, s_q, h_q, causal, scale, fp8)."""
         import torch
         import mla_paged_kv_fwd_amd as mla
         import workloads as W
 
         self.torch, self.mla, self.name = torch, mla, name
         (self.q, self.kc, self.bt, self.sl, self.s_q, self.h_q, self.causal, self.scale,
-         self.fp8) = W.make_config_device(name)
+         self.fp8) = inputs if inputs is not None else W.make_config_device(name)
         seqlens = self.sl.cpu().numpy()
         self.batch = seqlens.shape[0]
         self.bytes = W.algorithmic_bytes(seqlens, self.s_q, self.h_q, self.fp8)
@@ -202,6 +206,44 @@ def kv_write_bench(steps, warmup):
     return dict(kernel="kv_write_kernel<true>", rows=rows, us=round(us, 2), alg_bytes=alg,
                 gbs=round(alg / us / 1e3, 1), hbm_frac=round(alg / us / 1e3 / PEAK_HBM_GBS, 4),
                 bound="hbm", append_rows=2 * batch, append_us=round(us_append, 2))
+
+
+SWEEP_BATCH = (8, 32, 128)
+SWEEP_LEN = (1024, 4096, 16384)
+SWEEP_HQ = (16, 32, 64, 128)
+SWEEP_SQ = (1, 2, 4)
+
+
+def sweep(steps, warmup):
+    """Shape sweep over batch x sequence length x h_q x s_q (causal when
+    s_q > 1), bf16 cache, every request at the same length.  One JSON line per
+    shape: the whole step and the attention kernel back to back, with their
+    throughput and the kernel's fraction of its roofline."""
+    import math
+
+    import torch
+    import workloads as W
+
+    for batch in SWEEP_BATCH:
+        for length in SWEEP_LEN:
+            for h_q in SWEEP_HQ:
+                for s_q in SWEEP_SQ:
+                    sl = np.full(batch, length, dtype=np.int32)
+                    q, kc, bt, slt = W.make_device_inputs(sl, s_q, h_q, False, seed=batch + length + h_q)
+                    r = Runner(f"sweep b{batch} L{length} h{h_q} s{s_q}",
+                               (q, kc, bt, slt, s_q, h_q, s_q > 1, 1.0 / math.sqrt(W.D_QK), False))
+                    rep = r.report(r.measure(steps, warmup))
+                    a = rep["attn_kernel_us"] * 1e-6
+                    frac = max(rep["alg_bytes"] / a / (PEAK_HBM_GBS * 1e9),
+                               rep["alg_flops"] / a / (PEAK_BF16_TFLOPS * 1e12))
+                    print(json.dumps(dict(batch=batch, seqlen=length, h_q=h_q, s_q=s_q,
+                                          step_us=rep["us_per_step"],
+                                          attn_kernel_us=rep["attn_kernel_us"],
+                                          attn_gbs=rep["attn_gbs"], attn_tflops=rep["attn_tflops"],
+                                          bound=rep["bound"], attn_roofline_frac=round(frac, 4),
+                                          split_slots=rep["split_slots"])), flush=True)
+                    del r, q, kc, bt, slt
+                    torch.cuda.empty_cache()
 
 
 def fp8_accuracy():
@@ -356,6 +398,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
+    if args.sweep:
+        sweep(args.steps, args.warmup)
         return
     main_r = Runner(args.workload)
     m = main_r.measure(args.steps, args.warmup)

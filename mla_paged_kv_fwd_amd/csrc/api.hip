@@ -167,11 +167,11 @@ int mla_default_num_parts(int device, int s_q, int h_q) {
             return MLA_ERR_HIP;
         g_cu_count[device] = cus;
     }
-    // one work-group per CU: a part spans M / 64 work-groups in the 64-row
-    // kernel and M / 16 (run in several rounds) in the 16-row kernel
+    // one work-group per CU, all in one round: a part spans M / 64
+    // work-groups in the 64-row kernel and M / 16 in the 16-row kernel
     const int M = s_q * h_q;
     int parts = g_cu_count[device];
-    if (use_rows64(M)) parts = parts / (M / 64);
+    parts = parts / (M / (use_rows64(M) ? 64 : mla::decode_rows_per_group()));
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
 }

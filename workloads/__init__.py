@@ -197,15 +197,23 @@ def make_config_device(name, device="cuda"):
     seeded CUDA generator; N(0,1) rounded to bf16; shuffled physical pages).
     For timing runs, where regenerating gigabytes on the host would dominate.
     Returns (q, kcache, block_table, seqlens, s_q, h_q, causal, scale, fp8)."""
-    import torch
-
     cfg = CONFIGS[name]
     rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
     seqlens = config_seqlens(name, rng)
-    s_q, h_q, fp8 = cfg["s_q"], cfg["h_q"], cfg["fp8"]
+    q, kc, bt, sl = make_device_inputs(seqlens, cfg["s_q"], cfg["h_q"], cfg["fp8"], cfg["seed"],
+                                       device)
+    return q, kc, bt, sl, cfg["s_q"], cfg["h_q"], cfg["causal"], 1.0 / math.sqrt(D_QK), cfg["fp8"]
+
+
+def make_device_inputs(seqlens, s_q, h_q, fp8, seed, device="cuda"):
+    """Device-memory inputs of any shape: q, kcache (bf16 or FP8 records),
+    block_table (a seeded permutation of the physical pages) and seqlens."""
+    import torch
+
+    seqlens = np.asarray(seqlens, dtype=np.int32)
     batch = seqlens.shape[0]
     g = torch.Generator(device=device)
-    g.manual_seed(cfg["seed"])
+    g.manual_seed(seed)
     q = torch.randn((batch, s_q, h_q, D_QK), generator=g, device=device).to(torch.bfloat16)
     pages = (seqlens.astype(np.int64) + PAGE - 1) // PAGE
     n_pages = int(pages.sum())
@@ -236,4 +244,4 @@ def make_config_device(name, device="cuda"):
             kc[p0:p1, :, D_V:D_V + 16] = scale.contiguous().view(torch.uint8).reshape(p1 - p0, PAGE, 16)
             kc[p0:p1, :, D_V + 16:] = x[..., D_V:].to(torch.bfloat16).contiguous().view(torch.uint8)
     sl = torch.from_numpy(seqlens).to(device)
-    return q, kc, bt, sl, s_q, h_q, cfg["causal"], 1.0 / math.sqrt(D_QK), fp8
+    return q, kc, bt, sl
