@@ -28,8 +28,11 @@ static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::k
 namespace {
 
 // Kernel choice: 64 query rows per work-group with specialised score / value
-// waves when a request has at least 64 rows; 16 rows per work-group otherwise.
-bool use_rows64(int M) { return M >= 64; }
+// waves when a request has at least 32 rows (32 rows leave half the group as
+// padding: the problem is memory-bound and reads each page once instead of
+// twice); 16 rows per work-group otherwise.
+bool use_rows64(int M) { return M >= 32; }
+int rows64_groups(int M) { return (M + 63) / 64; }  // M = 32 pads one group
 
 bool shape_supported(int s_q, int h_q) {
     return (s_q == 1 || s_q == 2 || s_q == 4) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
@@ -89,7 +92,7 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.causal = causal;
     hipError_t e;
     if (use_rows64(M)) {
-        a.row_groups = M / 64;
+        a.row_groups = rows64_groups(M);
         e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
                            : mla::launch_decode_rows64(a, (hipStream_t)stream);
     } else {
@@ -171,7 +174,7 @@ int mla_default_num_parts(int device, int s_q, int h_q) {
     // work-groups in the 64-row kernel and M / 16 in the 16-row kernel
     const int M = s_q * h_q;
     int parts = g_cu_count[device];
-    parts = parts / (M / (use_rows64(M) ? 64 : mla::decode_rows_per_group()));
+    parts = parts / (use_rows64(M) ? rows64_groups(M) : M / mla::decode_rows_per_group());
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
 }

@@ -134,8 +134,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
 
     if (w < 2) {
         // ================= score waves: rows row0 + 32 w + (lane % 32)
+        // rows past M (M = 32 pads one 64-row group) repeat the last row's
+        // query and visibility; their results are not written
         const int row = row0 + 32 * w + l32;
-        const int qi = row / a.h_q;
+        const int row_q = row < a.M ? row : a.M - 1;
+        const int qi = row_q / a.h_q;
         const float c = a.scale_log2;  // > 0
         const float grow = kGrowLog2 / c;
         const int krec = kTokBytesFp8 * l32;  // this lane's K token record in a slot
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
             const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;
             // Q^T operand for 32x32x16: lane holds dims 16 ks + 8 h .. +8 of its row
             bf16x8 qf[kDQk / 16];
-            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row) * kDQk + 8 * h;
+            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row_q) * kDQk + 8 * h;
 #pragma unroll
             for (int ks = 0; ks < kDQk / 16; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
 #pragma unroll
@@ -291,10 +294,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                 stat_lds[kRowsWG + 32 * w + l32] = wsum;
                 const float lse_val =
                     lsum > 0.f ? (m * c + log2f(lsum)) * 0.69314718055994530942f : -INFINITY;
-                if (sg.nsplit == 1)
+                if (row >= a.M) {
+                } else if (sg.nsplit == 1) {
                     a.lse[(int64_t)sg.b * a.M + row] = lse_val;
-                else
+                } else {
                     a.lse_part[(int64_t)(split_base[sg.b] + sg.rank) * a.M + row] = lse_val;
+                }
             }
             __syncthreads();  // stats visible to the value waves
             __syncthreads();  // value waves have staged the output

@@ -76,12 +76,14 @@ __device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int3
 }
 
 // All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
-// segment's split slot (fp32), four threads per row, coalesced.
+// segment's split slot (fp32), four threads per row, coalesced.  Rows at or
+// past M (padding of a 32-row problem) are not written.
 __device__ __forceinline__ void write_rows(const DecodeArgs &a, const Segment &sg,
                                            const int32_t *split_base, const float *X,
                                            const float *row_sum, int row0, int tid) {
     const int r = tid >> 2, c0 = (tid & 3) * 128;
     const int orow = row0 + r;
+    if (orow >= a.M) return;
     const float *xr = X + r * kXStride + c0;
     const float lsum = row_sum[r];
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;

@@ -40,6 +40,9 @@ SHAPES = [
     ([5, 64, 257], 1, 128, False, True),
     ([1, 31, 32, 33, 63, 64, 65, 700], 1, 64, False, True),
     ([2, 66, 130, 400], 2, 128, True, True),
+    # 32 rows: run as one 64-row group with 32 padding rows
+    ([1, 63, 64, 65, 200, 1000], 2, 16, True, True),
+    ([3, 64, 190, 513], 1, 32, False, True),
     # four query tokens per request (multi-token prediction drafts)
     ([3, 4, 5, 64, 131, 700], 4, 16, True, False),
     ([3, 4, 5, 64, 131, 700], 4, 32, False, False),
@@ -70,6 +73,9 @@ GROWING = [
     ([300, 1000, 2100], 1, 128, False, 8, True),
     ([1000, 3000], 2, 32, True, 4, True),
     ([300, 1000, 2100], 4, 64, True, 8, False),
+    # 16 rows: the 16-row kernel's lazy rescale
+    ([300, 1000, 2100], 1, 16, False, 8, False),
+    ([300, 1000, 2100], 1, 16, False, 8, True),
 ]
 
 
@@ -132,6 +138,14 @@ def test_empty_requests_and_empty_causal_rows():
     ref_out, ref_lse = oracle_all(case)
     assert np.isneginf(ref_lse[0]).all() and np.isneginf(ref_lse[1, 0]).all()
     compare(out, lse, ref_out, ref_lse, "empty rows")
+
+
+def test_empty_requests_with_16_rows():
+    case = W.make_case([0, 5, 0, 130, 0], 1, 16, seed=18, spare_pages=1, poison=True)
+    out, lse = run_gpu(case, num_parts=8)
+    ref_out, ref_lse = oracle_all(case)
+    assert np.isneginf(ref_lse[0]).all() and np.isneginf(ref_lse[4]).all()
+    compare(out, lse, ref_out, ref_lse, "empty requests, 16 rows")
 
 
 def test_gpu_plan_equals_oracle_plan():
