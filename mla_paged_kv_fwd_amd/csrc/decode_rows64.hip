@@ -1,5 +1,5 @@
-// MLA decode attention for many query rows per request (s_q * h_q >= 64):
-// gfx950 kernel with specialised waves.
+// MLA decode attention for many query rows per request (s_q * h_q >= 32; 32
+// rows run as one 64-row group with padding rows): gfx950 kernel with specialised waves.
 //
 // A work-group (4 waves, one per SIMD) owns one split-KV part and one group of
 // 64 query rows.  It walks the part's pages in 32-token half-pages:

@@ -1,5 +1,5 @@
 // MLA decode attention over an FP8 latent cache for many query rows per
-// request (s_q * h_q >= 64): gfx950 kernel with specialised waves.
+// request (s_q * h_q >= 32, 32 rows padded to one 64-row group): gfx950 kernel with specialised waves.
 //
 // Cache record (656 bytes per token): 512 OCP E4M3FN codes of the latent
 // dims, four little-endian fp32 scales (one per 128-dim tile), 64 bf16 RoPE
