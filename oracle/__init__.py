@@ -62,6 +62,10 @@ def _load():
     lib.mla_oracle_kv_write.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P,
                                         ctypes.c_int, P]
     lib.mla_oracle_kv_write.restype = None
+    lib.mla_oracle_decode_sparse_rows.argtypes = [
+        P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int64, P, ctypes.c_int,
+        ctypes.c_double, P, ctypes.c_int64, P, P]
+    lib.mla_oracle_decode_sparse_rows.restype = None
     lib.mla_oracle_bf16_token_bytes.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -174,3 +178,29 @@ def kv_write(k_new, block_table, seqlens, cache, kind):
     _load().mla_oracle_kv_write(_ptr(k_new), batch, n_new, _ptr(bt), bt.shape[1], _ptr(sl),
                                 int(kind), _ptr(out))
     return out
+
+
+def decode_sparse(q, cache, kind, block_table, indices, scale, rows=None):
+    """Sparse decode: row (b, i, h) attends to the cached tokens listed in
+    indices[b, i, :] (int32 positions within request b; < 0 names nothing).
+    q uint16 [batch, s_q, h_q, 576].  Returns (out float64 [..., 512], lse
+    float64 [...]) for all rows, or for the listed (b, i, h) rows."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    batch, s_q, h_q = q.shape[:3]
+    cache = np.ascontiguousarray(cache)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    idx = np.ascontiguousarray(indices, dtype=np.int32).reshape(batch, s_q, -1)
+    topk = idx.shape[2]
+    whole = rows is None
+    if whole:
+        rows = all_rows(batch, s_q, h_q)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    out = np.zeros((rows.shape[0], D_V), dtype=np.float64)
+    lse = np.zeros((rows.shape[0],), dtype=np.float64)
+    lib.mla_oracle_decode_sparse_rows(_ptr(q), s_q, h_q, _ptr(cache), int(kind), _ptr(bt), bt.shape[1],
+                                      _ptr(idx), topk, float(scale), _ptr(rows), rows.shape[0],
+                                      _ptr(out), _ptr(lse))
+    if whole:
+        return out.reshape(batch, s_q, h_q, D_V), lse.reshape(batch, s_q, h_q)
+    return out, lse

@@ -272,6 +272,72 @@ int mla_oracle_decode_rows(const uint16_t *q, int s_q, int h_q, const void *cach
 }
 
 /*
+ * Sparse decode: query token i of request b attends only to the cached
+ * tokens its list names (DeepSeek KB page, "Key Contributions": the FP8
+ * cache serves a sparse decode kernel; the list itself comes from an indexer
+ * the pages do not describe).  indices int32 [batch][s_q][topk] holds token
+ * positions within the request; entries < 0 name nothing.  A listed position
+ * is used as given (a position listed twice counts twice).  Row (b, i, h)
+ * gets the textbook attention over the listed keys; a row whose list is
+ * empty gets out = 0, lse = -inf.
+ *   rows int32 [n_rows, 3] = (b, i, h); out double [n_rows, 512]; lse [n_rows]
+ */
+void mla_oracle_decode_sparse_rows(const uint16_t *q, int s_q, int h_q, const void *cache,
+                                   int kind, const int32_t *block_table, int64_t bt_stride,
+                                   const int32_t *indices, int topk, double scale,
+                                   const int32_t *rows, int64_t n_rows, double *out, double *lse)
+{
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < n_rows; ++r) {
+        int b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
+        const int32_t *list = indices + ((int64_t)b * s_q + i) * topk;
+        const uint16_t *qrow = q + (((int64_t)b * s_q + i) * h_q + h) * ORC_D_QK;
+        double qd[ORC_D_QK], kd[ORC_D_QK], *o = out + r * ORC_D_V;
+        double *score = (double *)malloc((size_t)(topk > 0 ? topk : 1) * sizeof(double));
+        double mx = -INFINITY, z = 0.0;
+        int k, d, n = 0;
+        for (d = 0; d < ORC_D_V; ++d)
+            o[d] = 0.0;
+        for (d = 0; d < ORC_D_QK; ++d)
+            qd[d] = orc_bf16(qrow[d]);
+        for (k = 0; k < topk; ++k) {
+            int64_t j = list[k], phys;
+            double dot = 0.0;
+            if (j < 0) continue;
+            phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
+            orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
+            for (d = 0; d < ORC_D_QK; ++d)
+                dot += qd[d] * kd[d];
+            score[n] = scale * dot;
+            if (score[n] > mx) mx = score[n];
+            ++n;
+        }
+        if (n == 0) {
+            lse[r] = -INFINITY;
+            free(score);
+            continue;
+        }
+        n = 0;
+        for (k = 0; k < topk; ++k) {
+            int64_t j = list[k], phys;
+            double w;
+            if (j < 0) continue;
+            phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
+            orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
+            w = exp(score[n++] - mx);
+            z += w;
+            for (d = 0; d < ORC_D_V; ++d)
+                o[d] += w * kd[d];
+        }
+        for (d = 0; d < ORC_D_V; ++d)
+            o[d] /= z;
+        lse[r] = mx + log(z);
+        free(score);
+    }
+}
+
+/*
  * Merge attention results computed over disjoint key sets of the same row.
  * Each part holds its own normalised output o_p and lse_p.  The merged lse is
  * ln sum_p exp(lse_p) and the merged output weights each part by
