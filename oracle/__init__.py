@@ -182,7 +182,8 @@ def kv_write(k_new, block_table, seqlens, cache, kind):
 
 def decode_sparse(q, cache, kind, block_table, indices, scale, rows=None):
     """Sparse decode: row (b, i, h) attends to the cached tokens listed in
-    indices[b, i, :] (int32 positions within request b; < 0 names nothing).
+    indices[b, i, :] (int32 positions within request b; the list ends at its
+    first negative entry).
     q uint16 [batch, s_q, h_q, 576].  Returns (out float64 [..., 512], lse
     float64 [...]) for all rows, or for the listed (b, i, h) rows."""
     lib = _load()

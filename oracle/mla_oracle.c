@@ -276,10 +276,11 @@ int mla_oracle_decode_rows(const uint16_t *q, int s_q, int h_q, const void *cach
  * tokens its list names (DeepSeek KB page, "Key Contributions": the FP8
  * cache serves a sparse decode kernel; the list itself comes from an indexer
  * the pages do not describe).  indices int32 [batch][s_q][topk] holds token
- * positions within the request; entries < 0 name nothing.  A listed position
- * is used as given (a position listed twice counts twice).  Row (b, i, h)
- * gets the textbook attention over the listed keys; a row whose list is
- * empty gets out = 0, lse = -inf.
+ * positions within the request; the list of query token (b, i) ends at its
+ * first negative entry (lists shorter than topk are padded with negatives).
+ * A listed position is used as given (a position listed twice counts twice).
+ * Row (b, i, h) gets the textbook attention over the listed keys; a row whose
+ * list is empty gets out = 0, lse = -inf.
  *   rows int32 [n_rows, 3] = (b, i, h); out double [n_rows, 512]; lse [n_rows]
  */
 void mla_oracle_decode_sparse_rows(const uint16_t *q, int s_q, int h_q, const void *cache,
@@ -304,7 +305,7 @@ void mla_oracle_decode_sparse_rows(const uint16_t *q, int s_q, int h_q, const vo
         for (k = 0; k < topk; ++k) {
             int64_t j = list[k], phys;
             double dot = 0.0;
-            if (j < 0) continue;
+            if (j < 0) break;
             phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
             orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
             for (d = 0; d < ORC_D_QK; ++d)
@@ -322,7 +323,7 @@ void mla_oracle_decode_sparse_rows(const uint16_t *q, int s_q, int h_q, const vo
         for (k = 0; k < topk; ++k) {
             int64_t j = list[k], phys;
             double w;
-            if (j < 0) continue;
+            if (j < 0) break;
             phys = block_table[(int64_t)b * bt_stride + j / ORC_PAGE];
             orc_key(cache, kind, phys, (int)(j % ORC_PAGE), kd);
             w = exp(score[n++] - mx);

@@ -9,16 +9,26 @@ import workloads as W
 from tests.test_oracle import _contiguous_keys, _q_rows, _sdpa
 
 
-def _lists(seqlens, s_q, topk, rng, holes=0.2, dup=False):
+def _lists(seqlens, s_q, topk, rng, dup=False):
+    """Random lists of random lengths, padded with -1 (and some junk after
+    the first -1, which must be ignored)."""
     idx = np.full((len(seqlens), s_q, topk), -1, dtype=np.int32)
     for b, L in enumerate(seqlens):
         for i in range(s_q):
             if L == 0:
                 continue
             pick = rng.integers(0, L, topk) if dup else rng.choice(L, size=min(topk, L), replace=False)
-            idx[b, i, :len(pick)] = pick
-            idx[b, i, rng.random(topk) < holes] = -1
+            n = int(rng.integers(0, len(pick) + 1))
+            idx[b, i, :n] = pick[:n]
+            if n + 1 < topk:
+                idx[b, i, n + 1:] = pick[n + 1:topk] if len(pick) >= topk else -1
     return idx
+
+
+def _listed(lst):
+    """The entries before the first negative one."""
+    neg = np.nonzero(lst < 0)[0]
+    return lst[: neg[0]] if len(neg) else lst
 
 
 def test_full_lists_equal_the_dense_decode():
@@ -59,7 +69,10 @@ def test_random_lists_match_sdpa_on_the_gathered_keys(fp8):
     for b in range(len(seqlens)):
         keys = _contiguous_keys(case, b)
         for i in range(s_q):
-            sel = idx[b, i][idx[b, i] >= 0]
+            sel = _listed(idx[b, i])
+            if len(sel) == 0:
+                assert np.all(out[b, i] == 0) and np.all(np.isneginf(lse[b, i]))
+                continue
             ro, rl = _sdpa(_q_rows(case, b, i), keys[sel], case.scale)
             np.testing.assert_allclose(out[b, i], ro, rtol=1e-10, atol=1e-12)
             np.testing.assert_allclose(lse[b, i], rl, rtol=1e-12, atol=1e-12)
@@ -68,9 +81,9 @@ def test_random_lists_match_sdpa_on_the_gathered_keys(fp8):
 def test_order_of_a_list_does_not_matter():
     rng = np.random.default_rng(54)
     case = W.make_case([500, 90], 1, 8, seed=55)
-    idx = _lists([500, 90], 1, 128, rng)
+    idx = np.stack([rng.choice(L, 80, replace=False) for L in (500, 90)]).astype(np.int32)[:, None]
     out, lse = oracle.decode_sparse(case.q, case.cache, 0, case.block_table, idx, case.scale)
-    perm = idx[:, :, rng.permutation(128)]
+    perm = idx[:, :, rng.permutation(80)]
     out2, lse2 = oracle.decode_sparse(case.q, case.cache, 0, case.block_table, perm, case.scale)
     np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-13)
@@ -79,7 +92,9 @@ def test_order_of_a_list_does_not_matter():
 def test_empty_and_single_entry_lists():
     case = W.make_case([40, 40], 1, 4, seed=56)
     idx = np.full((2, 1, 16), -1, dtype=np.int32)
-    idx[1, 0, 7] = 33                      # one listed token
+    idx[0, 0, 3] = 5                       # after the first -1: not listed
+    idx[1, 0, 0] = 33                      # one listed token
+    idx[1, 0, 5] = 7                       # after the first -1: not listed
     out, lse = oracle.decode_sparse(case.q, case.cache, 0, case.block_table, idx, case.scale)
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
     k = W.bf16_to_f32(case.cache[case.block_table[1, 0], 33]).astype(np.float64)
