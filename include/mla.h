@@ -174,6 +174,35 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
                               void *out, float *lse, void *stream);
 
 /*
+ * Sparse decode: query token i of request b attends only to the cached tokens
+ * its list names (DeepSeek KB page, "Key Contributions": the FP8 cache serves
+ * a sparse decode kernel; the list comes from an indexer the pages do not
+ * describe).
+ *   indices  int32 [batch][s_q][topk]: token positions within request b; the
+ *            list of (b, i) ends at its first negative entry (pad short lists
+ *            with -1).  A position listed twice counts twice.  Positions must
+ *            lie inside the request's cached length (caller's contract, like
+ *            block-table contents).
+ * Every head h of (b, i) attends over the listed keys (no causal mask: the
+ * list decides); a token whose list is empty gets out = 0, lse = -inf.
+ * The call gathers the listed rows (bf16) or records (FP8) into the
+ * workspace, plans num_parts parts over batch * s_q one-token problems of
+ * their list lengths, decodes them and merges the splits: one pass over
+ * topk tokens per query token instead of the whole cache.
+ *   kv_format 0 = bf16 cache, 1 = FP8 records; q, out, lse as for decode.
+ *   batch * s_q <= 16384; topk >= 1; num_parts as for mla_get_metadata
+ *   (mla_default_num_parts(device, 1, h_q) suits).
+ *   workspace >= mla_sparse_workspace_bytes(...) bytes, 256-byte aligned.
+ */
+size_t mla_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int kv_format,
+                                  int num_parts);
+mla_status mla_decode_sparse(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                             const int32_t *block_table, int block_table_stride,
+                             const int32_t *indices, int topk, int batch, int s_q, int h_q,
+                             float softmax_scale, int num_parts, void *workspace,
+                             size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
  * Cache writer: stores the rows of the newest n_new tokens of every request
  * in the paged cache.  Row i of request b (k_new[b][i]: 576 bf16 values, 512
  * latent then 64 RoPE) is the token at position L_b - n_new + i (seqlens count

@@ -13,7 +13,8 @@ import torch
 __all__ = [
     "MlaError", "lib", "D_QK", "D_V", "PAGE", "FP8_RECORD", "META_INTS",
     "default_num_parts", "plan_overhead", "workspace_bytes", "get_metadata",
-    "get_metadata_host", "decode", "decode_attn", "decode_combine", "kv_cache_write",
+    "get_metadata_host", "decode", "decode_attn", "decode_combine", "decode_sparse",
+    "sparse_workspace_bytes", "kv_cache_write",
     "status_string",
 ]
 
@@ -49,6 +50,9 @@ _SIGNATURES = {
                              _SZ, _P, _P, _P]),
     "mla_decode_combine": (_I, [_P, _I, _I, _I, _I, _P, _SZ, _P, _P, _P]),
     "mla_kv_cache_write": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
+    "mla_sparse_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "mla_decode_sparse": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _SZ, _P,
+                               _P, _P]),
     "mla_kv_cache_write_fp8": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
 }
 
@@ -231,3 +235,34 @@ def kv_cache_write(k_new, block_table, seqlens, kcache, fp8=False):
     _check(fn(_ptr(k_new), batch, n_new, _ptr(block_table), block_table.shape[1], _ptr(seqlens),
               _ptr(kcache), kcache.shape[0], _stream()), "mla_kv_cache_write")
     return kcache
+
+
+def sparse_workspace_bytes(batch, s_q, h_q, topk, num_parts, fp8=False):
+    return lib().mla_sparse_workspace_bytes(batch, s_q, h_q, topk, 1 if fp8 else 0, num_parts)
+
+
+def decode_sparse(q, kcache, block_table, indices, softmax_scale, fp8=False, num_parts=None,
+                  workspace=None, out=None, lse=None):
+    """Sparse decode: query token (b, i) attends to the tokens listed in
+    indices[b, i] (int32 [batch, s_q, topk] positions within request b; the
+    list ends at its first negative entry).  Returns (out bf16, lse fp32)."""
+    if indices.dtype != torch.int32 or indices.dim() != 3 or not indices.is_cuda or \
+            not indices.is_contiguous():
+        raise MlaError("indices must be a contiguous int32 CUDA tensor [batch, s_q, topk]")
+    b, s_q, h_q, _ = q.shape
+    if tuple(indices.shape[:2]) != (b, s_q):
+        raise MlaError("indices must be [batch, s_q, topk] for q's batch and s_q")
+    seqlens = torch.zeros((b,), dtype=torch.int32, device=q.device)  # not read: shape check only
+    _validate(q, kcache, block_table, seqlens, fp8)
+    topk = indices.shape[2]
+    if num_parts is None:
+        num_parts = default_num_parts(1, h_q, q.device.index)
+    need = sparse_workspace_bytes(b, s_q, h_q, topk, num_parts, fp8)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    out, lse = _outputs(q, out, lse)
+    _check(lib().mla_decode_sparse(
+        _ptr(q), _ptr(kcache), 1 if fp8 else 0, kcache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(indices), topk, b, s_q, h_q, float(softmax_scale), num_parts,
+        _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream()), "mla_decode_sparse")
+    return out, lse

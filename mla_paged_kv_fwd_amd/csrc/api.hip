@@ -17,6 +17,12 @@ hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const int32_t *block_table,
                            int64_t bt_stride, const int32_t *seqlens, void *cache, bool fp8,
                            hipStream_t stream);
+hipError_t launch_sparse_prep(const int32_t *indices, int rows, int topk, int pages_per,
+                              int32_t *lens, int32_t *gathered_bt, hipStream_t stream);
+hipError_t launch_sparse_gather(const unsigned char *kv, bool fp8, const int32_t *block_table,
+                                int64_t bt_stride, const int32_t *indices, int batch, int s_q,
+                                int topk, int pages_per, unsigned char *gathered,
+                                hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -130,6 +136,74 @@ mla_status kv_write_impl(const void *k_new, int batch, int n_new, const int32_t 
                                         block_table_stride, seqlens, kcache, fp8,
                                         (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// Sparse decode workspace: the gathered cache, its block table, the list
+// lengths, the plan, then the decode workspace of the one-token problems.
+struct SparseLayout {
+    size_t gathered, bt, lens, meta, split_base, decode_ws, decode_ws_bytes, total;
+};
+
+SparseLayout sparse_layout(int batch, int s_q, int h_q, int topk, int kv_format, int num_parts) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rows = (size_t)batch * s_q, pages = (size_t)(topk + mla::kPage - 1) / mla::kPage;
+    const size_t tok = kv_format == 1 ? mla::kTokBytesFp8 : mla::kTokBytesBf16;
+    SparseLayout L;
+    size_t off = 0;
+    L.gathered = off;
+    off += up(rows * pages * mla::kPage * tok);
+    L.bt = off;
+    off += up(rows * pages * 4);
+    L.lens = off;
+    off += up(rows * 4);
+    L.meta = off;
+    off += up((size_t)num_parts * mla::kMetaInts * 4);
+    L.split_base = off;
+    off += up((rows + 1) * 4);
+    L.decode_ws = off;
+    L.decode_ws_bytes = workspace_bytes((int)rows, 1, h_q, num_parts);
+    off += up(L.decode_ws_bytes);
+    L.total = off;
+    return L;
+}
+
+mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                              const int32_t *block_table, int block_table_stride,
+                              const int32_t *indices, int topk, int batch, int s_q, int h_q,
+                              float softmax_scale, int num_parts, void *workspace, size_t ws_bytes,
+                              void *out, float *lse, void *stream) {
+    if (!q || !kcache || !block_table || !indices || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (kv_format != 0 && kv_format != 1) return MLA_ERR_INVALID_ARG;
+    if (num_pages <= 0 || block_table_stride < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+    if (batch <= 0 || s_q <= 0 || h_q <= 0 || num_parts <= 0) return MLA_ERR_INVALID_ARG;
+    if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+    const int rows = batch * s_q;
+    mla_status st = check_plan_args(rows, 1, h_q, num_parts);
+    if (st != MLA_OK) return st;
+    const SparseLayout L = sparse_layout(batch, s_q, h_q, topk, kv_format, num_parts);
+    if (!workspace || ws_bytes < L.total || ((uintptr_t)workspace & 255) != 0)
+        return MLA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char *ws = (unsigned char *)workspace;
+    const int pages_per = (topk + mla::kPage - 1) / mla::kPage;
+    int32_t *lens = (int32_t *)(ws + L.lens), *bt = (int32_t *)(ws + L.bt);
+    int32_t *meta = (int32_t *)(ws + L.meta), *split_base = (int32_t *)(ws + L.split_base);
+    hipError_t e = mla::launch_sparse_prep(indices, rows, topk, pages_per, lens, bt, s);
+    if (e == hipSuccess)
+        e = mla::launch_sparse_gather((const unsigned char *)kcache, kv_format == 1, block_table,
+                                      block_table_stride, indices, batch, s_q, topk, pages_per,
+                                      ws + L.gathered, s);
+    if (e == hipSuccess)
+        e = mla::launch_plan(lens, rows, mla::plan_overhead(1, h_q), num_parts, meta, split_base, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    // the one-token problems: q, out and lse keep their memory layout
+    st = decode_attn_impl(q, ws + L.gathered, kv_format, (int64_t)rows * pages_per, bt, pages_per,
+                          lens, rows, 1, h_q, softmax_scale, 0, meta, split_base, num_parts,
+                          ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream);
+    if (st != MLA_OK) return st;
+    return combine_impl(split_base, rows, 1, h_q, num_parts, ws + L.decode_ws, L.decode_ws_bytes,
+                        out, lse, stream);
 }
 
 int g_cu_count[64];
@@ -252,6 +326,23 @@ mla_status mla_decode_fwd_fp8(const void *q, const void *kcache_fp8, int64_t num
     return decode_fwd(q, kcache_fp8, 1, num_pages, block_table, block_table_stride, seqlens, batch,
                       s_q, h_q, softmax_scale, causal, meta, split_base, num_parts, workspace,
                       workspace_bytes_, out, lse, stream);
+}
+
+size_t mla_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int kv_format,
+                                  int num_parts) {
+    if (batch <= 0 || s_q <= 0 || h_q <= 0 || topk <= 0 || num_parts <= 0) return 0;
+    if (kv_format != 0 && kv_format != 1) return 0;
+    return sparse_layout(batch, s_q, h_q, topk, kv_format, num_parts).total;
+}
+
+mla_status mla_decode_sparse(const void *q, const void *kcache, int kv_format, int64_t num_pages,
+                             const int32_t *block_table, int block_table_stride,
+                             const int32_t *indices, int topk, int batch, int s_q, int h_q,
+                             float softmax_scale, int num_parts, void *workspace,
+                             size_t workspace_bytes_, void *out, float *lse, void *stream) {
+    return decode_sparse_impl(q, kcache, kv_format, num_pages, block_table, block_table_stride,
+                              indices, topk, batch, s_q, h_q, softmax_scale, num_parts, workspace,
+                              workspace_bytes_, out, lse, stream);
 }
 
 mla_status mla_kv_cache_write(const void *k_new, int batch, int n_new,

@@ -122,6 +122,38 @@ def test_cache_writer_argument_errors(name):
     assert fn(FAKE, 16384, 1 << 17, FAKE, 4, FAKE, FAKE, 10, None) == UNSUPPORTED  # >= 2^31 rows
 
 
+def test_sparse_decode_argument_errors():
+    lib = load_lib()
+    fn = lib.mla_decode_sparse
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    sz = lib.mla_sparse_workspace_bytes
+    sz.restype = ctypes.c_size_t
+    sz.argtypes = [ctypes.c_int] * 6
+    need = sz(2, 1, 128, 2048, 1, 64)
+    assert need > 2 * 2048 * 656  # at least the gathered records
+    assert sz(0, 1, 128, 2048, 1, 64) == 0 and sz(2, 1, 128, 2048, 2, 64) == 0
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, fmt=1, pages=10, bt=FAKE, stride=4, idx=FAKE, topk=2048, batch=2,
+                 s_q=1, h_q=128, scale=0.04, parts=64, ws=ws, ws_bytes=need, out=FAKE, lse=FAKE)
+        a.update(kw)
+        return fn(a["q"], a["kc"], a["fmt"], a["pages"], a["bt"], a["stride"], a["idx"], a["topk"],
+                  a["batch"], a["s_q"], a["h_q"], a["scale"], a["parts"], a["ws"], a["ws_bytes"],
+                  a["out"], a["lse"], None)
+    assert call(idx=None) == INVALID
+    assert call(fmt=2) == INVALID
+    assert call(topk=0) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(h_q=48) == UNSUPPORTED
+    assert call(batch=8192, s_q=4) == UNSUPPORTED          # 32768 one-token problems
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE
+
+
 def _host_plan(lib, seqlens, s_q, h_q, parts):
     sl = np.ascontiguousarray(seqlens, dtype=np.int32)
     meta = np.full((parts, 8), 12345, dtype=np.int32)
