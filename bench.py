@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
-    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,fp8_accuracy",
+    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,sparse,fp8_accuracy",
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -246,6 +246,57 @@ def sweep(steps, warmup):
                     torch.cuda.empty_cache()
 
 
+def sparse_bench(steps, warmup):
+    """Sparse decode over the FP8 workload's cache (64 requests x 16384
+    tokens, h_q 128, s_q 1): each query token attends to 2048 distinct listed
+    tokens.  The whole call (prep, gather, plan, decode, combine) between two
+    events, launches back to back; FLOPs = 2 * h_q * (576 + 512) per listed
+    token and row; bytes = the listed records read once, plus q, out, lse and
+    the lists."""
+    import math
+
+    import torch
+    import mla_paged_kv_fwd_amd as mla
+    import workloads as W
+
+    q, kc, bt, sl, s_q, h_q, _, scale, _ = W.make_config_device("fp8")
+    batch, length, topk = q.shape[0], int(sl[0].item()), 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(79)
+    idx = torch.argsort(torch.rand((batch, s_q, length), generator=g, device="cuda"), dim=-1)[
+        ..., :topk].to(torch.int32).contiguous()
+    num_parts = mla.default_num_parts(1, h_q)
+    ws = torch.empty((mla.sparse_workspace_bytes(batch, s_q, h_q, topk, num_parts, fp8=True),),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((batch, s_q, h_q, W.D_V), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((batch, s_q, h_q), dtype=torch.float32, device="cuda")
+    lib = mla.lib()
+    stream = torch.cuda.current_stream()
+    args = (q.data_ptr(), kc.data_ptr(), 1, kc.shape[0], bt.data_ptr(), bt.shape[1], idx.data_ptr(),
+            topk, batch, s_q, h_q, float(scale), num_parts, ws.data_ptr(), ws.numel(),
+            out.data_ptr(), lse.data_ptr(), stream.cuda_stream)
+    for _ in range(warmup):
+        lib.mla_decode_sparse(*args)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(steps):
+        if lib.mla_decode_sparse(*args) != 0:
+            raise RuntimeError("mla_decode_sparse failed")
+    a1.record(stream)
+    torch.cuda.synchronize()
+    us = a0.elapsed_time(a1) / steps * 1e3
+    rows = batch * s_q
+    flops = 2 * h_q * (W.D_QK + W.D_V) * topk * rows
+    alg = rows * topk * (W.FP8_RECORD + 4) + rows * h_q * (2 * W.D_QK + 2 * W.D_V + 4)
+    res = dict(shape=f"batch {batch} x {length}, s_q {s_q}, h_q {h_q}, fp8 cache, {topk} listed tokens",
+               us=round(us, 2), alg_flops=flops, alg_bytes=alg, tflops=round(flops / us / 1e6, 1),
+               mfma_frac=round(flops / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+               gbs=round(alg / us / 1e3, 1))
+    del q, kc, bt, sl, idx, ws, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def fp8_accuracy():
     """FP8 cache against bf16 cache on the same latent: the FP8 workload's
     shape (64 requests x 16384 tokens, s_q 1, h_q 128), N(0,1) rows rounded to
@@ -409,8 +460,9 @@ def main():
     workloads = {args.workload: rep}
     del main_r
     for name in [x for x in args.extra.split(",") if x]:
-        if name in ("kvwrite", "fp8_accuracy"):
-            rep_x = kv_write_bench(args.steps, args.warmup) if name == "kvwrite" else fp8_accuracy()
+        if name in ("kvwrite", "fp8_accuracy", "sparse"):
+            rep_x = (kv_write_bench(args.steps, args.warmup) if name == "kvwrite" else
+                     sparse_bench(args.steps, args.warmup) if name == "sparse" else fp8_accuracy())
             print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
             workloads[name] = rep_x
             torch.cuda.empty_cache()
