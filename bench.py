@@ -419,7 +419,7 @@ def roofline(rep, workload):
     if rows < 64:
         kernel = "decode_rowgroup_kernel<%s>" % ("true" if cfg["fp8"] else "false")
     else:
-        kernel = "decode_rows64_fp8_kernel" if cfg["fp8"] else "decode_rows64_kernel"
+        kernel = "decode_rows64_fp8_kernel<false>" if cfg["fp8"] else "decode_rows64_kernel<false>"
     traffic = measured_traffic(kernel, workload)
     if rep["bound"] == "hbm":
         achieved, peak, unit = rep["attn_gbs"], PEAK_HBM_GBS, "GB/s"

@@ -19,10 +19,13 @@ hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const in
                            hipStream_t stream);
 hipError_t launch_sparse_prep(const int32_t *indices, int rows, int topk, int pages_per,
                               int32_t *lens, int32_t *gathered_bt, hipStream_t stream);
+hipError_t launch_sparse_ids(const int32_t *indices, const int32_t *block_table,
+                             int64_t bt_stride, int rows, int s_q, int topk, int tok_per,
+                             int32_t *lens, int32_t *ids, hipStream_t stream);
 hipError_t launch_sparse_gather(const unsigned char *kv, bool fp8, const int32_t *block_table,
-                                int64_t bt_stride, const int32_t *indices, int batch, int s_q,
-                                int topk, int pages_per, unsigned char *gathered,
-                                hipStream_t stream);
+                                int64_t bt_stride, const int32_t *indices, const int32_t *lens,
+                                int batch, int s_q, int topk, int pages_per,
+                                unsigned char *gathered, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -62,7 +65,8 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
                             const int32_t *seqlens, int batch, int s_q, int h_q,
                             float softmax_scale, int causal, const int32_t *meta,
                             const int32_t *split_base, int num_parts, void *workspace,
-                            size_t ws_bytes, void *out, float *lse, void *stream) {
+                            size_t ws_bytes, void *out, float *lse, void *stream,
+                            int token_list = 0) {
     if (!q || !kcache || !block_table || !seqlens || !meta || !split_base || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (kv_format != 0 && kv_format != 1) return MLA_ERR_INVALID_ARG;
@@ -96,6 +100,8 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.num_parts = num_parts;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
+    a.token_list = token_list;
+    if (token_list && !use_rows64(M)) return MLA_ERR_UNSUPPORTED;
     hipError_t e;
     if (use_rows64(M)) {
         a.row_groups = rows64_groups(M);
@@ -138,8 +144,13 @@ mla_status kv_write_impl(const void *k_new, int batch, int n_new, const int32_t 
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-// Sparse decode workspace: the gathered cache, its block table, the list
-// lengths, the plan, then the decode workspace of the one-token problems.
+// Sparse decode: the 64-row kernels (h_q >= 32) read the listed rows in
+// place through per-list token ids; the 16-row kernel decodes a gathered copy.
+bool sparse_token_ids(int h_q) { return use_rows64(h_q); }
+
+// Sparse decode workspace: the token ids (64-row kernels) or the gathered
+// cache and its block table (16-row kernel), the list lengths, the plan, then
+// the decode workspace of the one-token problems.
 struct SparseLayout {
     size_t gathered, bt, lens, meta, split_base, decode_ws, decode_ws_bytes, total;
 };
@@ -151,9 +162,9 @@ SparseLayout sparse_layout(int batch, int s_q, int h_q, int topk, int kv_format,
     SparseLayout L;
     size_t off = 0;
     L.gathered = off;
-    off += up(rows * pages * mla::kPage * tok);
-    L.bt = off;
-    off += up(rows * pages * 4);
+    if (!sparse_token_ids(h_q)) off += up(rows * pages * mla::kPage * tok);
+    L.bt = off;  // token ids [rows][64 pages] or the gathered block table [rows][pages]
+    off += up(rows * pages * (sparse_token_ids(h_q) ? mla::kPage : 1) * 4);
     L.lens = off;
     off += up(rows * 4);
     L.meta = off;
@@ -187,20 +198,34 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
     hipStream_t s = (hipStream_t)stream;
     unsigned char *ws = (unsigned char *)workspace;
     const int pages_per = (topk + mla::kPage - 1) / mla::kPage;
+    const bool token_ids = sparse_token_ids(h_q);
+    // token ids are int32: page * 64 + slot must stay below 2^31
+    if (token_ids && num_pages > 0x7FFFFFFFLL / mla::kPage) return MLA_ERR_UNSUPPORTED;
     int32_t *lens = (int32_t *)(ws + L.lens), *bt = (int32_t *)(ws + L.bt);
     int32_t *meta = (int32_t *)(ws + L.meta), *split_base = (int32_t *)(ws + L.split_base);
-    hipError_t e = mla::launch_sparse_prep(indices, rows, topk, pages_per, lens, bt, s);
-    if (e == hipSuccess)
-        e = mla::launch_sparse_gather((const unsigned char *)kcache, kv_format == 1, block_table,
-                                      block_table_stride, indices, batch, s_q, topk, pages_per,
-                                      ws + L.gathered, s);
+    hipError_t e;
+    if (token_ids) {
+        e = mla::launch_sparse_ids(indices, block_table, block_table_stride, rows, s_q, topk,
+                                   pages_per * mla::kPage, lens, bt, s);
+    } else {
+        e = mla::launch_sparse_prep(indices, rows, topk, pages_per, lens, bt, s);
+        if (e == hipSuccess)
+            e = mla::launch_sparse_gather((const unsigned char *)kcache, kv_format == 1,
+                                          block_table, block_table_stride, indices, lens, batch,
+                                          s_q, topk, pages_per, ws + L.gathered, s);
+    }
     if (e == hipSuccess)
         e = mla::launch_plan(lens, rows, mla::plan_overhead(1, h_q), num_parts, meta, split_base, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     // the one-token problems: q, out and lse keep their memory layout
-    st = decode_attn_impl(q, ws + L.gathered, kv_format, (int64_t)rows * pages_per, bt, pages_per,
-                          lens, rows, 1, h_q, softmax_scale, 0, meta, split_base, num_parts,
-                          ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream);
+    if (token_ids)
+        st = decode_attn_impl(q, kcache, kv_format, num_pages, bt, pages_per * mla::kPage, lens,
+                              rows, 1, h_q, softmax_scale, 0, meta, split_base, num_parts,
+                              ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream, 1);
+    else
+        st = decode_attn_impl(q, ws + L.gathered, kv_format, (int64_t)rows * pages_per, bt,
+                              pages_per, lens, rows, 1, h_q, softmax_scale, 0, meta, split_base,
+                              num_parts, ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream);
     if (st != MLA_OK) return st;
     return combine_impl(split_base, rows, 1, h_q, num_parts, ws + L.decode_ws, L.decode_ws_bytes,
                         out, lse, stream);

@@ -42,6 +42,7 @@ struct DecodeArgs {
     int row_groups;             // M / rows per work-group
     float scale_log2;           // softmax_scale * log2(e)
     int causal;
+    int token_list;             // 64-row kernels: block_table holds token-id lists
 };
 
 // Split-KV plan: work of one part, computed identically on host and device

@@ -16,6 +16,11 @@
 // t-1, and half-pages t+1, t+2 are in flight.  One work-group barrier per step.
 //
 // The half-page LDS layout and the operand addressing are in halfpage_bf16.h.
+//
+// Token-list mode (sparse decode, kList): each "request" is one query token's
+// list of cache token ids; the score waves stage the ids of half-page t + 3 in
+// LDS during step t, and the value waves load each listed row straight from
+// its page, so the listed rows are read once, from the cache itself.
 #include <math.h>
 
 #include "common.h"
@@ -35,7 +40,8 @@ constexpr int kPOff = kRing * kHalfBytes;         // P hand-off: 2 x (2 row tile
 constexpr int kPBytes = 4096;
 constexpr int kFlagOff = kPOff + 2 * kPBytes;     // restart flags of the two score waves
 constexpr int kStatOff = kFlagOff + 64;           // final (m, l) per row
-constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
+constexpr int kIdsOff = kStatOff + 2 * kRowsWG * 4;  // token-list mode: ids of kRing half-pages
+constexpr int kLdsBytes = kIdsOff + kRing * kHalf * 4;
 
 // Value wave v's share of a half-page: the 18 one-KB blocks (G, lam) with
 // G = 2 v + g2, each one 128-byte line (lam = 0..8) of eight tokens.
@@ -48,26 +54,37 @@ struct HalfDma {
     }
 };
 
-// Value wave v's direct-to-LDS loads of half-page t of a segment.
+// Value wave v's direct-to-LDS loads of half-page t of a segment: from its
+// page, or (token-list mode) from the rows whose ids sit in LDS slot t % kRing.
+template <bool kList>
 __device__ __forceinline__ HalfDma half_dma(const Segment &sg, const unsigned char *kv, int t, int v,
-                                            int lane, unsigned ring0) {
-    const int j = sg.j0 + (t >> 1);
-    const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
-    const int64_t phys = sg.bt[j];
+                                            int lane, unsigned ring0, const lds_i32 *ids) {
     HalfDma d;
-    d.src[0] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v, lane);
-    d.src[1] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v + 1, lane);
+    if constexpr (kList) {
+        const lds_i32 *id = ids + (t % kRing) * kHalf;
+        const int tok_last = sg.tok_last(t);
+        d.src[0] = halfpage::dma_row_ids(kv, id, tok_last, 2 * v, lane);
+        d.src[1] = halfpage::dma_row_ids(kv, id, tok_last, 2 * v + 1, lane);
+    } else {
+        const int j = sg.j0 + (t >> 1);
+        const int tok_last = (j == sg.npages - 1) ? (sg.L - 1 - j * kPage) : (kPage - 1);
+        const int64_t phys = sg.bt[j];
+        d.src[0] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v, lane);
+        d.src[1] = halfpage::dma_row(kv, phys, (t & 1) * kHalf, tok_last, 2 * v + 1, lane);
+    }
     d.dst = ring0 + (t % kRing) * kHalfBytes;
     return d;
 }
 
+template <bool kList>
 __device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
-                                           int lane, unsigned ring0) {
-    const HalfDma d = half_dma(sg, kv, t, v, lane, ring0);
+                                           int lane, unsigned ring0, const lds_i32 *ids) {
+    const HalfDma d = half_dma<kList>(sg, kv, t, v, lane, ring0, ids);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) d.issue(v, k);
 }
 
+template <bool kList>
 __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
     const DecodeArgs a, const uint16_t *__restrict__ q, const unsigned char *__restrict__ kv,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seqlens,
@@ -95,6 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
     volatile __attribute__((address_space(3))) int *flag_lds =
         (volatile __attribute__((address_space(3))) int *)(smem + kFlagOff);
     float *stat_lds = (float *)(smem_raw + kStatOff);
+    lds_i32 *ids_lds = (lds_i32 *)(smem + kIdsOff);
     float *X = (float *)smem_raw;  // output stage [64][kXStride], over the ring
     const int row0 = rg * kRowsWG;
 
@@ -110,6 +128,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         int kofs[4];  // K operand of k-step ks for this lane
         halfpage::k_offsets(kofs, l32, h);
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            if constexpr (kList) {
+                stage_first_ids(ids_lds, sg, l32, h);
+                __syncthreads();  // the value waves load half-pages 0 .. 2
+            }
             int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
             n_visible = n_visible > 0 ? n_visible : 0;
             const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;  // every row sees these
@@ -156,6 +178,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         again = __builtin_amdgcn_readfirstlane(f0 | f1) != 0;
                         break;
                     }
+                    // token-list mode: ids of half-page t + 3, into LDS at the
+                    // end of this step (the value waves issue its loads in
+                    // step t + 1)
+                    const bool stage = kList && t + 3 < sg.H;
+                    int id_next = 0;
+                    if (stage) id_next = list_ids(sg, t + 3)[l32];
                     const lds_u8 *S = smem + (t % kRing) * kHalfBytes;
                     f32x16 sacc = {};
                     constexpr int kPre = 8;  // K fragments in flight ahead of the MFMAs
@@ -222,8 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                         (u32x4){pk[0], pk[1], pk[2], pk[3]};
                     *(u32x4 __attribute__((address_space(3))) *)(P + (2 * w + 1) * 1024 + lane * 16) =
                         (u32x4){pk[4], pk[5], pk[6], pk[7]};
+                    if (stage && h == 0) ids_lds[((t + 3) % kRing) * kHalf + l32] = id_next;
                 }
                 if (again) {
+                    if constexpr (kList) stage_first_ids(ids_lds, sg, l32, h);
                     wait_vmcnt<0>();
                     __syncthreads();
                 }
@@ -252,8 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
         int vofs[2][2];  // transposed V reads of this wave's 256 dims
         halfpage::v_offsets(vofs, lane, 4 * v);
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
-            issue_step(sg, kv, 0, v, lane, ring0);
-            if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+            if constexpr (kList) __syncthreads();  // ids of half-pages 0 .. 2 staged
+            issue_step<kList>(sg, kv, 0, v, lane, ring0, ids_lds);
+            if (sg.H > 1) issue_step<kList>(sg, kv, 1, v, lane, ring0, ids_lds);
             f32x16 o[2][8];
             bool again;
             do {  // one pass over the segment; repeated only after a restart
@@ -269,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     }
                     const bool more = t + 2 < sg.H;
                     if (t == 0) {
-                        if (more) issue_step(sg, kv, t + 2, v, lane, ring0);
+                        if (more) issue_step<kList>(sg, kv, t + 2, v, lane, ring0, ids_lds);
                         continue;
                     }
                     // Half-page t + 2 goes to the slot half-page t - 2 used; its
@@ -279,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                     const lds_u8 *V = smem + (tp % kRing) * kHalfBytes;
                     const lds_u8 *P = smem + kPOff + (tp & 1) * kPBytes;
                     HalfDma dma;
-                    if (more) dma = half_dma(sg, kv, t + 2, v, lane, ring0);
+                    if (more) dma = half_dma<kList>(sg, kv, t + 2, v, lane, ring0, ids_lds);
                     auto read_v = [&](int kk, int dt) { return halfpage::read_v(V, vofs, kk, dt); };
                     auto read_p = [&](int blk) {
                         return *(const bf16x8 __attribute__((address_space(3))) *)(P + blk * 1024 + lane * 16);
@@ -312,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
                 if (again) {
                     wait_vmcnt<0>();
                     __syncthreads();
-                    issue_step(sg, kv, 0, v, lane, ring0);
-                    if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+                    issue_step<kList>(sg, kv, 0, v, lane, ring0, ids_lds);
+                    if (sg.H > 1) issue_step<kList>(sg, kv, 1, v, lane, ring0, ids_lds);
                 }
             } while (again);
             __syncthreads();  // score waves' final stats visible
@@ -330,8 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_kernel(
 hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream) {
     const int groups8 = (a.num_parts + 7) / 8;
     const dim3 grid(groups8 * 8 * a.row_groups), block(kThreads);
-    hipLaunchKernelGGL(decode_rows64_kernel, grid, block, 0, stream, a, a.q, a.kv, a.block_table,
-                       a.seqlens, a.meta, a.split_base);
+    if (a.token_list)
+        hipLaunchKernelGGL(decode_rows64_kernel<true>, grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
+    else
+        hipLaunchKernelGGL(decode_rows64_kernel<false>, grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
     return hipGetLastError();
 }
 

@@ -27,6 +27,11 @@
 // (164 dwords, 36 mod 64 banks) both the ds_read_b64 K reads of 16 tokens and
 // the transposed V reads of 8 tokens hit distinct banks, so no swizzle is
 // needed.
+//
+// Token-list mode (sparse decode, kList): each "request" is one query token's
+// list of cache token ids; the score waves stage the ids of half-page t + 3 in
+// LDS during step t, and each direct-to-LDS load takes its record from the
+// cache page the id names, so the listed records are read once, in place.
 #include <math.h>
 
 #include "common.h"
@@ -49,7 +54,8 @@ constexpr int kPBytes = 4096;                          // P^T: 2 row tiles x 2 k
 constexpr int kXBytes = kRowsWG * kXStride * 4;        // output stage, over ring and P
 constexpr int kFlagOff = (kPOff + 2 * kPBytes) > kXBytes ? (kPOff + 2 * kPBytes) : kXBytes;
 constexpr int kStatOff = kFlagOff + 64;
-constexpr int kLdsBytes = kStatOff + 2 * kRowsWG * 4;
+constexpr int kIdsOff = kStatOff + 2 * kRowsWG * 4;  // token-list mode: ids of kRing half-pages
+constexpr int kLdsBytes = kIdsOff + kRing * kHalf * 4;
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -69,43 +75,70 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(unsigned lo, unsigned hi) {
     return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Value wave v's direct-to-LDS loads of a half-page: 1 KB block i covers
-// bytes [1024 i, 1024 i + 1024) of the 32 records; lane l takes chunk
-// 64 i + l, moved to the same chunk of record tok_last when it lies past it.
-struct HalfDmaFp8 {
-    const unsigned char *hp;  // first record of the half-page
-    unsigned dst;             // LDS byte address of the slot
-    int tok_last;
-    __device__ __forceinline__ void issue(int i, int lane) const {
-        int ch = 64 * i + lane;
-        const int tau = ch / kChunks;
-        if (tau > tok_last) ch = kChunks * tok_last + (ch - kChunks * tau);
-        dma16(hp + 16 * ch, __builtin_amdgcn_readfirstlane(dst + 1024 * i));
-    }
-};
-
-__device__ __forceinline__ HalfDmaFp8 half_dma(const Segment &sg, const unsigned char *kv, int t,
-                                               unsigned ring0) {
-    const int j = sg.j0 + (t >> 1);
-    HalfDmaFp8 d;
-    d.hp = kv + ((int64_t)sg.bt[j] * kPage + (t & 1) * kHalf) * kTokBytesFp8;
-    d.dst = ring0 + (t % kRing) * kSlot;
-    d.tok_last = sg.tok_last(t);
-    return d;
-}
-
 // Blocks of value wave v: 0 .. 10 (v = 0) or 10 .. 20 (v = 1).  Both waves
 // load block 10 (the same bytes to the same place), which keeps their code
 // identical.
 __device__ __forceinline__ int first_block(int v) { return v ? kDmaFp8 - kDmaWave : 0; }
 
-__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
-                                           int lane, unsigned ring0) {
-    const HalfDmaFp8 d = half_dma(sg, kv, t, ring0);
+// Value wave v's direct-to-LDS loads of a half-page: its k-th load is 1 KB
+// block i = first_block(v) + k, bytes [1024 i, 1024 i + 1024) of the 32
+// records; lane l takes chunk 64 i + l, i.e. chunk c = 64 i + l - 41 tau of
+// record tau = (64 i + l) / 41, moved to the same chunk of record tok_last
+// when tau lies past it.  Record tau is at hp + 656 tau in paged mode, at
+// kv + 656 id[tau] in token-list mode (id[k] keeps this lane's id for load k).
+template <bool kList>
+struct HalfDmaFp8 {
+    const unsigned char *hp;  // paged: first record of the half-page; list: the cache
+    unsigned dst;             // LDS byte address of the slot
+    int tok_last, i0;
+    int id[kList ? kDmaWave : 1];
+    __device__ __forceinline__ void issue(int k, int lane) const {
+        const int i = i0 + k;
+        int ch = 64 * i + lane;
+        const int tau = ch / kChunks;
+        const unsigned char *src;
+        if constexpr (kList) {
+            src = hp + (int64_t)id[k] * kTokBytesFp8 + 16 * (ch - kChunks * tau);
+        } else {
+            if (tau > tok_last) ch = kChunks * tok_last + (ch - kChunks * tau);
+            src = hp + 16 * ch;
+        }
+        dma16(src, __builtin_amdgcn_readfirstlane(dst + 1024 * i));
+    }
+};
+
+template <bool kList>
+__device__ __forceinline__ HalfDmaFp8<kList> half_dma(const Segment &sg, const unsigned char *kv,
+                                                      int t, int v, int lane, unsigned ring0,
+                                                      const lds_i32 *ids) {
+    HalfDmaFp8<kList> d;
+    d.dst = ring0 + (t % kRing) * kSlot;
+    d.tok_last = sg.tok_last(t);
+    d.i0 = first_block(v);
+    if constexpr (kList) {
+        d.hp = kv;
+        const lds_i32 *id = ids + (t % kRing) * kHalf;
 #pragma unroll
-    for (int k = 0; k < kDmaWave; ++k) d.issue(first_block(v) + k, lane);
+        for (int k = 0; k < kDmaWave; ++k) {
+            const int tau = (64 * (d.i0 + k) + lane) / kChunks;
+            d.id[k] = id[tau < d.tok_last ? tau : d.tok_last];
+        }
+    } else {
+        const int j = sg.j0 + (t >> 1);
+        d.hp = kv + ((int64_t)sg.bt[j] * kPage + (t & 1) * kHalf) * kTokBytesFp8;
+    }
+    return d;
 }
 
+template <bool kList>
+__device__ __forceinline__ void issue_step(const Segment &sg, const unsigned char *kv, int t, int v,
+                                           int lane, unsigned ring0, const lds_i32 *ids) {
+    const HalfDmaFp8<kList> d = half_dma<kList>(sg, kv, t, v, lane, ring0, ids);
+#pragma unroll
+    for (int k = 0; k < kDmaWave; ++k) d.issue(k, lane);
+}
+
+template <bool kList>
 __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
     const DecodeArgs a, const uint16_t *__restrict__ q, const unsigned char *__restrict__ kv,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seqlens,
@@ -129,6 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
     volatile __attribute__((address_space(3))) int *flag_lds =
         (volatile __attribute__((address_space(3))) int *)(smem + kFlagOff);
     float *stat_lds = (float *)(smem_raw + kStatOff);
+    lds_i32 *ids_lds = (lds_i32 *)(smem + kIdsOff);
     float *X = (float *)smem_raw;  // output stage [64][kXStride]
     const int row0 = rg * kRowsWG;
 
@@ -143,6 +177,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
         const float grow = kGrowLog2 / c;
         const int krec = kTokBytesFp8 * l32;  // this lane's K token record in a slot
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
+            if constexpr (kList) {
+                stage_first_ids(ids_lds, sg, l32, h);
+                __syncthreads();  // the value waves load half-pages 0 .. 2
+            }
             int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
             n_visible = n_visible > 0 ? n_visible : 0;
             const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;
@@ -180,6 +218,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         again = __builtin_amdgcn_readfirstlane(f0 | f1) != 0;
                         break;
                     }
+                    // token-list mode: ids of half-page t + 3, into LDS at the
+                    // end of this step (the value waves issue its loads in
+                    // step t + 1)
+                    const bool stage = kList && t + 3 < sg.H;
+                    int id_next = 0;
+                    if (stage) id_next = list_ids(sg, t + 3)[l32];
                     const lds_u8 *S = smem + (t % kRing) * kSlot;
                     // S^T (32 tokens x 32 rows) per 128-dim tile and for the RoPE dims
                     f32x16 acc[5] = {};
@@ -282,8 +326,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         *(lds_u32x4 *)(P + kk * 1024) = pw;
                     }
                     wsum += rsum;
+                    if (stage && h == 0) ids_lds[((t + 3) % kRing) * kHalf + l32] = id_next;
                 }
                 if (again) {
+                    if constexpr (kList) stage_first_ids(ids_lds, sg, l32, h);
                     wait_vmcnt<0>();
                     __syncthreads();
                 }
@@ -322,8 +368,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
         // scales of tiles 2 v, 2 v + 1 of this lane's first token (4 (lane / 32))
         const int vsc = kTokBytesFp8 * (4 * (lane >> 5)) + kFp8ScalesAt + 8 * v;
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
-            issue_step(sg, kv, 0, v, lane, ring0);
-            if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+            if constexpr (kList) __syncthreads();  // ids of half-pages 0 .. 2 staged
+            issue_step<kList>(sg, kv, 0, v, lane, ring0, ids_lds);
+            if (sg.H > 1) issue_step<kList>(sg, kv, 1, v, lane, ring0, ids_lds);
             f32x16 o[2][8];
             bool again;
             do {  // one pass over the segment; repeated only after a restart
@@ -339,15 +386,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     }
                     const bool more = t + 2 < sg.H;
                     if (t == 0) {
-                        if (more) issue_step(sg, kv, t + 2, v, lane, ring0);
+                        if (more) issue_step<kList>(sg, kv, t + 2, v, lane, ring0, ids_lds);
                         continue;
                     }
                     // half-page t + 2 goes to the slot half-page t - 2 used; its
                     // loads are spread over this step's MFMAs (one after each
                     // MFMA pair)
-                    HalfDmaFp8 dma;
-                    if (more) dma = half_dma(sg, kv, t + 2, ring0);
-                    const int i0 = first_block(v);
+                    HalfDmaFp8<kList> dma;
+                    if (more) dma = half_dma<kList>(sg, kv, t + 2, v, lane, ring0, ids_lds);
                     const int tp = t - 1;  // half-page processed this step
                     const lds_u8 *V = smem + (tp % kRing) * kSlot + vrec;
                     const lds_u8 *Vs = smem + (tp % kRing) * kSlot + vsc;
@@ -390,20 +436,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p00, o[0][dt], 0, 0, 0);
                         o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p10, o[1][dt], 0, 0, 0);
                         v1[dt] = read_v(1, dt, sc1);
-                        if (more) dma.issue(i0 + dt, lane);
+                        if (more) dma.issue(dt, lane);
                     }
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) {
                         o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p01, o[0][dt], 0, 0, 0);
                         o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p11, o[1][dt], 0, 0, 0);
-                        if (more && dt < kDmaWave - 8) dma.issue(i0 + 8 + dt, lane);
+                        if (more && dt < kDmaWave - 8) dma.issue(8 + dt, lane);
                     }
                 }
                 if (again) {
                     wait_vmcnt<0>();
                     __syncthreads();
-                    issue_step(sg, kv, 0, v, lane, ring0);
-                    if (sg.H > 1) issue_step(sg, kv, 1, v, lane, ring0);
+                    issue_step<kList>(sg, kv, 0, v, lane, ring0, ids_lds);
+                    if (sg.H > 1) issue_step<kList>(sg, kv, 1, v, lane, ring0, ids_lds);
                 }
             } while (again);
             __syncthreads();  // score waves' final stats visible
@@ -420,8 +466,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
 hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream) {
     const int groups8 = (a.num_parts + 7) / 8;
     const dim3 grid(groups8 * 8 * a.row_groups), block(kThreads);
-    hipLaunchKernelGGL(decode_rows64_fp8_kernel, grid, block, 0, stream, a, a.q, a.kv,
-                       a.block_table, a.seqlens, a.meta, a.split_base);
+    if (a.token_list)
+        hipLaunchKernelGGL(decode_rows64_fp8_kernel<true>, grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
+    else
+        hipLaunchKernelGGL(decode_rows64_fp8_kernel<false>, grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
     return hipGetLastError();
 }
 

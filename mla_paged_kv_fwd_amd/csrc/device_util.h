@@ -6,6 +6,7 @@
 namespace mla {
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) int lds_i32;
 
 __device__ __forceinline__ unsigned lds_addr(const lds_u8 *p) { return (unsigned)(uintptr_t)p; }
 

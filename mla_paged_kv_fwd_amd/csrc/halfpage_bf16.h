@@ -42,6 +42,17 @@ __device__ __forceinline__ const unsigned char *dma_row(const unsigned char *kv,
     return kv + (phys * kPage + t) * kTokBytesBf16 + 16 * (b ^ swz(tau));
 }
 
+// The same loads when the half-page's tokens are listed by cache token id
+// (ids[tau] = page * 64 + slot of token tau of the half-page, in LDS).
+__device__ __forceinline__ const unsigned char *dma_row_ids(const unsigned char *kv,
+                                                            const lds_i32 *ids, int tok_last,
+                                                            int G, int lane) {
+    const int a = lane >> 3, b = lane & 7;
+    const int tau = 8 * G + a;
+    const int t = tau < tok_last ? tau : tok_last;
+    return kv + (int64_t)ids[t] * kTokBytesBf16 + 16 * (b ^ swz(tau));
+}
+
 // K operand of 32x32x16 k-step ks (A operand: lane = token l32, 8 dims
 // 16 ks + 8 h .. + 8): byte offset kofs[ks % 4] + 1024 (ks / 4).
 __device__ __forceinline__ void k_offsets(int (&kofs)[4], int l32, int h) {

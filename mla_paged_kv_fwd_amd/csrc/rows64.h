@@ -75,6 +75,26 @@ __device__ __forceinline__ void for_each_segment(const int32_t *mrow, const int3
     }
 }
 
+// Token-list mode (sparse decode).  A "request" is then one query token's
+// list of cache token ids (physical page * 64 + slot, in list order), and the
+// block-table argument holds these lists, bt_stride ids apart: half-page u of
+// a segment covers list positions 64 j0 + 32 u .. + 31.  The score waves copy
+// the ids of a half-page into LDS slot u % kRing before the value waves issue
+// its loads, which then address each token's row by its id.
+__device__ __forceinline__ const int32_t *list_ids(const Segment &sg, int u) {
+    return sg.bt + sg.j0 * kPage + u * kHalf;
+}
+
+// Ids of half-pages 0, 1, 2 (those the value waves load before the first
+// step's barrier) into their LDS slots; lanes 0..31 of a score wave.
+__device__ __forceinline__ void stage_first_ids(lds_i32 *ids, const Segment &sg, int l32, int h) {
+    if (h == 0) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            if (u < sg.H) ids[u * kHalf + l32] = list_ids(sg, u)[l32];
+    }
+}
+
 // All 256 threads: the staged [64][kXStride] fp32 output -> out (bf16) or the
 // segment's split slot (fp32), four threads per row, coalesced.  Rows at or
 // past M (padding of a 32-row problem) are not written.

@@ -133,7 +133,11 @@ def test_sparse_decode_argument_errors():
     sz.restype = ctypes.c_size_t
     sz.argtypes = [ctypes.c_int] * 6
     need = sz(2, 1, 128, 2048, 1, 64)
-    assert need > 2 * 2048 * 656  # at least the gathered records
+    dec = (2 + 64) * 128 * 513 * 4  # the one-token problems' split partials
+    # h_q >= 32 reads the records in place: token ids (4 B per list entry) only
+    assert dec + 2 * 2048 * 4 <= need < dec + 2 * 2048 * 4 + 8192
+    # h_q = 16 decodes a gathered copy: at least the gathered records
+    assert sz(2, 1, 16, 2048, 1, 64) > 2 * 2048 * 656
     assert sz(0, 1, 128, 2048, 1, 64) == 0 and sz(2, 1, 128, 2048, 2, 64) == 0
     ws = ctypes.c_void_p(0x100000)
 
@@ -152,6 +156,8 @@ def test_sparse_decode_argument_errors():
     assert call(batch=8192, s_q=4) == UNSUPPORTED          # 32768 one-token problems
     assert call(ws_bytes=need - 1) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE
+    # token ids are int32: page * 64 + slot must stay below 2^31
+    assert call(pages=(2**31 - 1) // 64 + 1) == UNSUPPORTED
 
 
 def _host_plan(lib, seqlens, s_q, h_q, parts):

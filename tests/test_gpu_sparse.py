@@ -54,6 +54,7 @@ CASES = [
     ([700, 2100, 130], 2, 128, 200, False),
     ([700, 2100, 130], 1, 128, 200, True),
     ([4000, 50], 4, 64, 512, True),
+    ([300, 5, 1000, 64], 4, 16, 333, True),
 ]
 
 
@@ -67,6 +68,23 @@ def test_sparse_decode_matches_oracle(seqlens, s_q, h_q, topk, fp8):
     ref, ref_lse = oracle.decode_sparse(case.q, case.cache, case.kind, case.block_table, idx,
                                         case.scale)
     compare(out, lse, ref, ref_lse, f"sparse {seqlens} h_q={h_q} topk={topk} fp8={fp8}")
+
+
+@pytest.mark.parametrize("h_q,fp8", [(128, False), (64, True), (16, False), (32, True)])
+def test_sparse_growing_scores_restart(h_q, fp8):
+    # RoPE keys scaled up along the sequence and lists in ascending order, so
+    # each row's running max keeps rising along its list: the 64-row kernels
+    # restart segments (staging the first token ids again), the 16-row kernel
+    # rescales
+    rng = np.random.default_rng(66 + h_q)
+    seqlens = [3000, 1200]
+    case = W.make_case(seqlens, 2, h_q, seed=67 + h_q, fp8=fp8, spare_pages=1, poison=True,
+                       rope_ramp=0.05)
+    idx = np.sort(_lists(seqlens, 2, 900, rng, full=True), axis=-1)
+    out, lse = _run(case, idx, num_parts=3)
+    ref, ref_lse = oracle.decode_sparse(case.q, case.cache, case.kind, case.block_table, idx,
+                                        case.scale)
+    compare(out, lse, ref, ref_lse, f"sparse growing h_q={h_q} fp8={fp8}")
 
 
 @pytest.mark.parametrize("num_parts", [1, 7, 256])
