@@ -86,13 +86,14 @@ __device__ __forceinline__ int first_block(int v) { return v ? kDmaFp8 - kDmaWav
 // record tau = (64 i + l) / 41, moved to the same chunk of record tok_last
 // when tau lies past it.  Record tau is at hp + 656 tau in paged mode, at
 // kv + 656 id[tau] in token-list mode (id[k] keeps this lane's id for load k).
+// i0 = first_block(v) comes from the call site, where it is a known scalar.
 template <bool kList>
 struct HalfDmaFp8 {
     const unsigned char *hp;  // paged: first record of the half-page; list: the cache
     unsigned dst;             // LDS byte address of the slot
-    int tok_last, i0;
+    int tok_last;
     int id[kList ? kDmaWave : 1];
-    __device__ __forceinline__ void issue(int k, int lane) const {
+    __device__ __forceinline__ void issue(int i0, int k, int lane) const {
         const int i = i0 + k;
         int ch = 64 * i + lane;
         const int tau = ch / kChunks;
@@ -114,13 +115,12 @@ __device__ __forceinline__ HalfDmaFp8<kList> half_dma(const Segment &sg, const u
     HalfDmaFp8<kList> d;
     d.dst = ring0 + (t % kRing) * kSlot;
     d.tok_last = sg.tok_last(t);
-    d.i0 = first_block(v);
     if constexpr (kList) {
         d.hp = kv;
         const lds_i32 *id = ids + (t % kRing) * kHalf;
 #pragma unroll
         for (int k = 0; k < kDmaWave; ++k) {
-            const int tau = (64 * (d.i0 + k) + lane) / kChunks;
+            const int tau = (64 * (first_block(v) + k) + lane) / kChunks;
             d.id[k] = id[tau < d.tok_last ? tau : d.tok_last];
         }
     } else {
@@ -135,7 +135,7 @@ __device__ __forceinline__ void issue_step(const Segment &sg, const unsigned cha
                                            int lane, unsigned ring0, const lds_i32 *ids) {
     const HalfDmaFp8<kList> d = half_dma<kList>(sg, kv, t, v, lane, ring0, ids);
 #pragma unroll
-    for (int k = 0; k < kDmaWave; ++k) d.issue(k, lane);
+    for (int k = 0; k < kDmaWave; ++k) d.issue(first_block(v), k, lane);
 }
 
 template <bool kList>
@@ -394,6 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     // MFMA pair)
                     HalfDmaFp8<kList> dma;
                     if (more) dma = half_dma<kList>(sg, kv, t + 2, v, lane, ring0, ids_lds);
+                    const int i0 = first_block(v);
                     const int tp = t - 1;  // half-page processed this step
                     const lds_u8 *V = smem + (tp % kRing) * kSlot + vrec;
                     const lds_u8 *Vs = smem + (tp % kRing) * kSlot + vsc;
@@ -436,13 +437,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p00, o[0][dt], 0, 0, 0);
                         o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0[dt], p10, o[1][dt], 0, 0, 0);
                         v1[dt] = read_v(1, dt, sc1);
-                        if (more) dma.issue(dt, lane);
+                        if (more) dma.issue(i0, dt, lane);
                     }
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) {
                         o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p01, o[0][dt], 0, 0, 0);
                         o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1[dt], p11, o[1][dt], 0, 0, 0);
-                        if (more && dt < kDmaWave - 8) dma.issue(8 + dt, lane);
+                        if (more && dt < kDmaWave - 8) dma.issue(i0, 8 + dt, lane);
                     }
                 }
                 if (again) {
