@@ -187,12 +187,11 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
  * list decides); a token whose list is empty gets out = 0, lse = -inf.
  * The call plans num_parts parts over batch * s_q one-token problems of
  * their list lengths, decodes them and merges the splits: one pass over the
- * listed tokens per query token instead of the whole cache.  For h_q >= 32
- * the decode reads each listed row (bf16) or record (FP8) in place through
- * per-list token ids (needs num_pages * 64 < 2^31, else
- * MLA_ERR_UNSUPPORTED); for h_q = 16 it first gathers the listed rows or
- * records into the workspace.  Entries at or past the first negative one
- * are never dereferenced.
+ * listed tokens per query token instead of the whole cache.  The decode
+ * reads each listed row (bf16) or record (FP8) in place, through per-list
+ * token ids (page * 64 + slot, int32: needs num_pages * 64 < 2^31, else
+ * MLA_ERR_UNSUPPORTED).  Entries at or past the first negative one are
+ * never dereferenced.
  *   kv_format 0 = bf16 cache, 1 = FP8 records; q, out, lse as for decode.
  *   batch * s_q <= 16384; topk >= 1; num_parts as for mla_get_metadata
  *   (mla_default_num_parts(device, 1, h_q) suits).

@@ -17,15 +17,9 @@ hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const int32_t *block_table,
                            int64_t bt_stride, const int32_t *seqlens, void *cache, bool fp8,
                            hipStream_t stream);
-hipError_t launch_sparse_prep(const int32_t *indices, int rows, int topk, int pages_per,
-                              int32_t *lens, int32_t *gathered_bt, hipStream_t stream);
 hipError_t launch_sparse_ids(const int32_t *indices, const int32_t *block_table,
                              int64_t bt_stride, int rows, int s_q, int topk, int tok_per,
                              int32_t *lens, int32_t *ids, hipStream_t stream);
-hipError_t launch_sparse_gather(const unsigned char *kv, bool fp8, const int32_t *block_table,
-                                int64_t bt_stride, const int32_t *indices, const int32_t *lens,
-                                int batch, int s_q, int topk, int pages_per,
-                                unsigned char *gathered, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -101,9 +95,9 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
     a.token_list = token_list;
-    if (token_list && !use_rows64(M)) return MLA_ERR_UNSUPPORTED;
     hipError_t e;
-    if (use_rows64(M)) {
+    // token lists always run on the 64-row kernels (M = 16 pads one group)
+    if (use_rows64(M) || token_list) {
         a.row_groups = rows64_groups(M);
         e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
                            : mla::launch_decode_rows64(a, (hipStream_t)stream);
@@ -144,27 +138,20 @@ mla_status kv_write_impl(const void *k_new, int batch, int n_new, const int32_t 
     return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-// Sparse decode: the 64-row kernels (h_q >= 32) read the listed rows in
-// place through per-list token ids; the 16-row kernel decodes a gathered copy.
-bool sparse_token_ids(int h_q) { return use_rows64(h_q); }
-
-// Sparse decode workspace: the token ids (64-row kernels) or the gathered
-// cache and its block table (16-row kernel), the list lengths, the plan, then
-// the decode workspace of the one-token problems.
+// Sparse decode workspace: the token ids [rows][64 * pages], the list
+// lengths, the plan, then the decode workspace of the one-token problems.
 struct SparseLayout {
-    size_t gathered, bt, lens, meta, split_base, decode_ws, decode_ws_bytes, total;
+    size_t ids, lens, meta, split_base, decode_ws, decode_ws_bytes, total;
 };
 
 SparseLayout sparse_layout(int batch, int s_q, int h_q, int topk, int kv_format, int num_parts) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)batch * s_q, pages = (size_t)(topk + mla::kPage - 1) / mla::kPage;
-    const size_t tok = kv_format == 1 ? mla::kTokBytesFp8 : mla::kTokBytesBf16;
+    (void)kv_format;  // the records are read in place: the layout is the same for both
     SparseLayout L;
     size_t off = 0;
-    L.gathered = off;
-    if (!sparse_token_ids(h_q)) off += up(rows * pages * mla::kPage * tok);
-    L.bt = off;  // token ids [rows][64 pages] or the gathered block table [rows][pages]
-    off += up(rows * pages * (sparse_token_ids(h_q) ? mla::kPage : 1) * 4);
+    L.ids = off;
+    off += up(rows * pages * mla::kPage * 4);
     L.lens = off;
     off += up(rows * 4);
     L.meta = off;
@@ -198,34 +185,19 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
     hipStream_t s = (hipStream_t)stream;
     unsigned char *ws = (unsigned char *)workspace;
     const int pages_per = (topk + mla::kPage - 1) / mla::kPage;
-    const bool token_ids = sparse_token_ids(h_q);
     // token ids are int32: page * 64 + slot must stay below 2^31
-    if (token_ids && num_pages > 0x7FFFFFFFLL / mla::kPage) return MLA_ERR_UNSUPPORTED;
-    int32_t *lens = (int32_t *)(ws + L.lens), *bt = (int32_t *)(ws + L.bt);
+    if (num_pages > 0x7FFFFFFFLL / mla::kPage) return MLA_ERR_UNSUPPORTED;
+    int32_t *lens = (int32_t *)(ws + L.lens), *ids = (int32_t *)(ws + L.ids);
     int32_t *meta = (int32_t *)(ws + L.meta), *split_base = (int32_t *)(ws + L.split_base);
-    hipError_t e;
-    if (token_ids) {
-        e = mla::launch_sparse_ids(indices, block_table, block_table_stride, rows, s_q, topk,
-                                   pages_per * mla::kPage, lens, bt, s);
-    } else {
-        e = mla::launch_sparse_prep(indices, rows, topk, pages_per, lens, bt, s);
-        if (e == hipSuccess)
-            e = mla::launch_sparse_gather((const unsigned char *)kcache, kv_format == 1,
-                                          block_table, block_table_stride, indices, lens, batch,
-                                          s_q, topk, pages_per, ws + L.gathered, s);
-    }
+    hipError_t e = mla::launch_sparse_ids(indices, block_table, block_table_stride, rows, s_q,
+                                          topk, pages_per * mla::kPage, lens, ids, s);
     if (e == hipSuccess)
         e = mla::launch_plan(lens, rows, mla::plan_overhead(1, h_q), num_parts, meta, split_base, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     // the one-token problems: q, out and lse keep their memory layout
-    if (token_ids)
-        st = decode_attn_impl(q, kcache, kv_format, num_pages, bt, pages_per * mla::kPage, lens,
-                              rows, 1, h_q, softmax_scale, 0, meta, split_base, num_parts,
-                              ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream, 1);
-    else
-        st = decode_attn_impl(q, ws + L.gathered, kv_format, (int64_t)rows * pages_per, bt,
-                              pages_per, lens, rows, 1, h_q, softmax_scale, 0, meta, split_base,
-                              num_parts, ws + L.decode_ws, L.decode_ws_bytes, out, lse, stream);
+    st = decode_attn_impl(q, kcache, kv_format, num_pages, ids, pages_per * mla::kPage, lens, rows,
+                          1, h_q, softmax_scale, 0, meta, split_base, num_parts, ws + L.decode_ws,
+                          L.decode_ws_bytes, out, lse, stream, 1);
     if (st != MLA_OK) return st;
     return combine_impl(split_base, rows, 1, h_q, num_parts, ws + L.decode_ws, L.decode_ws_bytes,
                         out, lse, stream);

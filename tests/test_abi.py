@@ -133,11 +133,12 @@ def test_sparse_decode_argument_errors():
     sz.restype = ctypes.c_size_t
     sz.argtypes = [ctypes.c_int] * 6
     need = sz(2, 1, 128, 2048, 1, 64)
-    dec = (2 + 64) * 128 * 513 * 4  # the one-token problems' split partials
-    # h_q >= 32 reads the records in place: token ids (4 B per list entry) only
-    assert dec + 2 * 2048 * 4 <= need < dec + 2 * 2048 * 4 + 8192
-    # h_q = 16 decodes a gathered copy: at least the gathered records
-    assert sz(2, 1, 16, 2048, 1, 64) > 2 * 2048 * 656
+    # the records are read in place: token ids (4 B per list entry), lengths,
+    # plan and the one-token problems' split partials, for any h_q and format
+    for h_q in (16, 128):
+        dec = (2 + 64) * h_q * 513 * 4
+        assert dec + 2 * 2048 * 4 <= sz(2, 1, h_q, 2048, 1, 64) < dec + 2 * 2048 * 4 + 8192
+    assert sz(2, 1, 128, 2048, 0, 64) == need
     assert sz(0, 1, 128, 2048, 1, 64) == 0 and sz(2, 1, 128, 2048, 2, 64) == 0
     ws = ctypes.c_void_p(0x100000)
 

@@ -74,8 +74,8 @@ def test_sparse_decode_matches_oracle(seqlens, s_q, h_q, topk, fp8):
 def test_sparse_growing_scores_restart(h_q, fp8):
     # RoPE keys scaled up along the sequence and lists in ascending order, so
     # each row's running max keeps rising along its list: the 64-row kernels
-    # restart segments (staging the first token ids again), the 16-row kernel
-    # rescales
+    # restart segments, staging the first token ids again (h_q = 16 and 32
+    # run as one padded 64-row group)
     rng = np.random.default_rng(66 + h_q)
     seqlens = [3000, 1200]
     case = W.make_case(seqlens, 2, h_q, seed=67 + h_q, fp8=fp8, spare_pages=1, poison=True,
