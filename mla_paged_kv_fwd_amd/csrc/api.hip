@@ -192,7 +192,10 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
     hipError_t e = mla::launch_sparse_ids(indices, block_table, block_table_stride, rows, s_q,
                                           topk, pages_per * mla::kPage, lens, ids, s);
     if (e == hipSuccess)
-        e = mla::launch_plan(lens, rows, mla::plan_overhead(1, h_q), num_parts, meta, split_base, s);
+        // no overhead units: full lists are equally long, and a list split over
+        // two parts pays its fixed cost in both, so equal page shares balance
+        // the parts (with c units per list, one half got c pages fewer)
+        e = mla::launch_plan(lens, rows, 0, num_parts, meta, split_base, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     // the one-token problems: q, out and lse keep their memory layout
     st = decode_attn_impl(q, kcache, kv_format, num_pages, ids, pages_per * mla::kPage, lens, rows,
