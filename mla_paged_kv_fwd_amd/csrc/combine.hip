@@ -30,20 +30,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const int d = (threadIdx.x & 63) * 8;
     uint16_t *dst = out + ((int64_t)b * M + r) * kDV + d;
 
-    // Every slot's lse and partial output are loaded up front, four slots at a
-    // time, so that the loads of a request overlap instead of waiting on one
-    // another.  A slot with lse = -inf gets weight 0 whatever it holds.
+    // Slots are merged four at a time: a chunk's lse values and partial
+    // outputs are loaded together, then merged into a running (max, sum,
+    // output) with a rescale when the max grows, so each chunk costs one
+    // memory round trip.  A slot with lse = -inf gets weight 0 whatever it
+    // holds.
     const float *lrow = lse_part + (int64_t)base * M + r;
     const float *orow = o_part + ((int64_t)base * M + r) * kDV + d;
     const int64_t ostride = (int64_t)M * kDV;
-    float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lrow[(int64_t)s * M]);
-    if (mx == -INFINITY) {  // no pages, or no visible key in any slot
-        *(u32x4 *)dst = (u32x4){0u, 0u, 0u, 0u};
-        if (d == 0) lse[(int64_t)b * M + r] = -INFINITY;
-        return;
-    }
-    float z = 0.f;
+    float mx = -INFINITY, z = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < ns; s0 += 4) {
         float ls[4];
@@ -55,6 +50,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
             v0[k] = *(const f32x4 *)(orow + s * ostride);
             v1[k] = *(const f32x4 *)(orow + s * ostride + 4);
         }
+        const float mc = fmaxf(fmaxf(ls[0], ls[1]), fmaxf(ls[2], ls[3]));
+        if (mc == -INFINITY) continue;  // no keys in this chunk
+        const float mn = fmaxf(mx, mc);
+        const float sc = expf(mx - mn);  // 0 while nothing has been merged
+        z *= sc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= sc;
+        mx = mn;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float e = expf(ls[k] - mx);  // 0 for an empty slot
@@ -65,6 +68,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
                 acc[4 + j] += ls[k] == -INFINITY ? 0.f : e * v1[k][j];
             }
         }
+    }
+    if (mx == -INFINITY) {  // no pages, or no visible key in any slot
+        *(u32x4 *)dst = (u32x4){0u, 0u, 0u, 0u};
+        if (d == 0) lse[(int64_t)b * M + r] = -INFINITY;
+        return;
     }
     const float lse_all = mx + logf(z);
     const float inv_z = 1.f / z;
