@@ -138,6 +138,7 @@ def get_metadata_host(seqlens, s_q, h_q, num_parts):
 
 
 def _validate(q, kcache, block_table, seqlens, fp8):
+    """Dtypes, shapes and placement of the inputs (seqlens may be None)."""
     if q.dtype != torch.bfloat16 or q.dim() != 4 or q.shape[-1] != D_QK:
         raise MlaError("q must be bf16 [batch, s_q, h_q, 576]")
     if fp8:
@@ -148,19 +149,29 @@ def _validate(q, kcache, block_table, seqlens, fp8):
             raise MlaError("kcache must be bf16 [pages, 64, 576]")
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise MlaError("block_table must be int32 [batch, width]")
-    if seqlens.dtype != torch.int32 or seqlens.dim() != 1:
+    if seqlens is not None and (seqlens.dtype != torch.int32 or seqlens.dim() != 1):
         raise MlaError("seqlens must be int32 [batch]")
     for t in (q, kcache, block_table, seqlens):
+        if t is None:
+            continue
         if not t.is_cuda or not t.is_contiguous():
             raise MlaError("all tensors must be contiguous CUDA tensors")
 
 
 def _outputs(q, out, lse):
+    """The caller's out / lse after checks, or new ones: the kernels write
+    every element, so a wrong shape would be a write out of bounds."""
     b, s_q, h_q, _ = q.shape
     if out is None:
         out = torch.empty((b, s_q, h_q, D_V), dtype=torch.bfloat16, device=q.device)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != (b, s_q, h_q, D_V)
+          or not out.is_cuda or not out.is_contiguous()):
+        raise MlaError("out must be a contiguous bf16 CUDA tensor [batch, s_q, h_q, 512]")
     if lse is None:
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (b, s_q, h_q)
+          or not lse.is_cuda or not lse.is_contiguous()):
+        raise MlaError("lse must be a contiguous fp32 CUDA tensor [batch, s_q, h_q]")
     return out, lse
 
 
@@ -252,8 +263,9 @@ def decode_sparse(q, kcache, block_table, indices, softmax_scale, fp8=False, num
     b, s_q, h_q, _ = q.shape
     if tuple(indices.shape[:2]) != (b, s_q):
         raise MlaError("indices must be [batch, s_q, topk] for q's batch and s_q")
-    seqlens = torch.zeros((b,), dtype=torch.int32, device=q.device)  # not read: shape check only
-    _validate(q, kcache, block_table, seqlens, fp8)
+    _validate(q, kcache, block_table, None, fp8)
+    if block_table.shape[0] != b:
+        raise MlaError("block_table must have one row per request")
     topk = indices.shape[2]
     if num_parts is None:
         num_parts = default_num_parts(1, h_q, q.device.index)
