@@ -235,6 +235,33 @@ mla_status mla_kv_cache_write_fp8(const void *k_new, int batch, int n_new,
                                   const int32_t *seqlens, void *kcache_fp8, int64_t num_pages,
                                   void *stream);
 
+/*
+ * Device-side checks of the caller's device data.  The decode, sparse and
+ * writer calls take block-table contents, lengths and list entries on trust
+ * (like any paged-attention kernel); these calls verify them on the device,
+ * reading only table entries inside the table, so they are safe on the very
+ * inputs they reject.  Each writes result (device, 2 x uint64, 8-byte
+ * aligned) on `stream`; read it after synchronising:
+ *   result[0]  number of bad requests (mla_check_block_table) or bad lists
+ *              (mla_check_sparse_indices); 0 if all is well
+ *   result[1]  smallest (request_or_list << 32) | where over the bad ones,
+ *              ~0 if none.  where = first bad logical page (a table entry
+ *              outside [0, num_pages)), first bad list position (its page
+ *              is past the table's width or its entry is outside the pool),
+ *              or 0xFFFFFFFF for a length that is negative or needs more
+ *              than block_table_stride pages.  A list is b * s_q + i.
+ * mla_check_block_table covers pages 0 .. ceil(L_b / 64) - 1 of each request;
+ * mla_check_sparse_indices covers entries before each list's first negative
+ * one.  Two kernels on `stream`; graph-capturable; argument errors as for
+ * the decode calls.
+ */
+mla_status mla_check_block_table(const int32_t *seqlens, int batch, const int32_t *block_table,
+                                 int block_table_stride, int64_t num_pages, uint64_t *result,
+                                 void *stream);
+mla_status mla_check_sparse_indices(const int32_t *block_table, int block_table_stride,
+                                    int64_t num_pages, const int32_t *indices, int topk,
+                                    int batch, int s_q, uint64_t *result, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

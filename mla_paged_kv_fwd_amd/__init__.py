@@ -54,6 +54,8 @@ _SIGNATURES = {
     "mla_decode_sparse": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _SZ, _P,
                                _P, _P]),
     "mla_kv_cache_write_fp8": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
+    "mla_check_block_table": (_I, [_P, _I, _P, _I, _I64, _P, _P]),
+    "mla_check_sparse_indices": (_I, [_P, _I, _I64, _P, _I, _I, _I, _P, _P]),
 }
 
 
@@ -206,10 +208,60 @@ def decode_combine(split_base, num_parts, workspace, out, lse):
     return out, lse
 
 
+def _checks_enabled():
+    """MLA_CHECK=1 in the environment runs the device-side input checks
+    before each decode, sparse decode and cache write (one synchronisation
+    each); off by default."""
+    return os.environ.get("MLA_CHECK", "") not in ("", "0")
+
+
+def _check_result(res):
+    v = [int(x) & 0xFFFFFFFFFFFFFFFF for x in res.cpu().tolist()]
+    if v[0] == 0:
+        return 0, None
+    where = v[1] & 0xFFFFFFFF
+    return v[0], (v[1] >> 32, None if where == 0xFFFFFFFF else where)
+
+
+def check_block_table(block_table, seqlens, num_pages):
+    """Device-side check that every request's length fits the table and every
+    block-table entry it uses is a page of the pool.  Synchronises.
+
+    Returns (bad_requests, first) with first = None, or (request, logical
+    page) for the smallest bad request; the page is None for a bad length."""
+    res = torch.empty((2,), dtype=torch.int64, device=block_table.device)
+    _check(lib().mla_check_block_table(_ptr(seqlens), seqlens.shape[0], _ptr(block_table),
+                                       block_table.shape[1], int(num_pages), _ptr(res), _stream()),
+           "mla_check_block_table")
+    return _check_result(res)
+
+
+def check_sparse_indices(block_table, indices, num_pages):
+    """Device-side check that every list entry before its list's end names a
+    logical page inside the table whose entry is a page of the pool.
+    Synchronises.  Returns (bad_lists, first) with first = None, or
+    (list b * s_q + i, list position) for the smallest bad list."""
+    b, s_q, topk = indices.shape
+    res = torch.empty((2,), dtype=torch.int64, device=indices.device)
+    _check(lib().mla_check_sparse_indices(_ptr(block_table), block_table.shape[1], int(num_pages),
+                                          _ptr(indices), topk, b, s_q, _ptr(res), _stream()),
+           "mla_check_sparse_indices")
+    return _check_result(res)
+
+
+def _raise_if_bad(result, what):
+    n, first = result
+    if n:
+        raise MlaError(f"{what}: {n} bad, first at {first}")
+
+
 def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, split_base=None,
            num_parts=None, workspace=None, out=None, lse=None, fp8=False):
     """MLA decode: returns (out bf16 [b, s_q, h_q, 512], lse fp32 [b, s_q, h_q])."""
     _validate(q, kcache, block_table, seqlens, fp8)
+    if _checks_enabled():
+        _raise_if_bad(check_block_table(block_table, seqlens, kcache.shape[0]),
+                      "block table / seqlens")
     b, s_q, h_q, _ = q.shape
     if meta is None:
         meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts)
@@ -242,6 +294,9 @@ def kv_cache_write(k_new, block_table, seqlens, kcache, fp8=False):
         if not t.is_cuda or not t.is_contiguous():
             raise MlaError("all tensors must be contiguous CUDA tensors")
     batch, n_new = k_new.shape[0], k_new.shape[1]
+    if _checks_enabled():
+        _raise_if_bad(check_block_table(block_table, seqlens, kcache.shape[0]),
+                      "block table / seqlens")
     fn = lib().mla_kv_cache_write_fp8 if fp8 else lib().mla_kv_cache_write
     _check(fn(_ptr(k_new), batch, n_new, _ptr(block_table), block_table.shape[1], _ptr(seqlens),
               _ptr(kcache), kcache.shape[0], _stream()), "mla_kv_cache_write")
@@ -266,6 +321,8 @@ def decode_sparse(q, kcache, block_table, indices, softmax_scale, fp8=False, num
     _validate(q, kcache, block_table, None, fp8)
     if block_table.shape[0] != b:
         raise MlaError("block_table must have one row per request")
+    if _checks_enabled():
+        _raise_if_bad(check_sparse_indices(block_table, indices, kcache.shape[0]), "sparse lists")
     topk = indices.shape[2]
     if num_parts is None:
         num_parts = default_num_parts(1, h_q, q.device.index)

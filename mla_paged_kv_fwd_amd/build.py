@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["api.hip", "plan.hip", "decode.hip", "decode_rows64.hip", "decode_rows64_fp8.hip",
-           "combine.hip", "kv_write.hip", "sparse.hip"]
+           "combine.hip", "kv_write.hip", "sparse.hip", "check.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

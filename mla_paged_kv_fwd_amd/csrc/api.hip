@@ -20,6 +20,12 @@ hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const in
 hipError_t launch_sparse_ids(const int32_t *indices, const int32_t *block_table,
                              int64_t bt_stride, int rows, int s_q, int topk, int tok_per,
                              int32_t *lens, int32_t *ids, hipStream_t stream);
+hipError_t launch_check_block_table(const int32_t *seqlens, int batch, const int32_t *block_table,
+                                    int64_t bt_stride, int64_t num_pages,
+                                    unsigned long long *result, hipStream_t stream);
+hipError_t launch_check_sparse(const int32_t *block_table, int64_t bt_stride, int64_t num_pages,
+                               const int32_t *indices, int rows, int s_q, int topk,
+                               unsigned long long *result, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
 }  // namespace mla
@@ -359,6 +365,31 @@ mla_status mla_kv_cache_write_fp8(const void *k_new, int batch, int n_new,
                                   void *stream) {
     return kv_write_impl(k_new, batch, n_new, block_table, block_table_stride, seqlens,
                          kcache_fp8, num_pages, true, stream);
+}
+
+mla_status mla_check_block_table(const int32_t *seqlens, int batch, const int32_t *block_table,
+                                 int block_table_stride, int64_t num_pages, uint64_t *result,
+                                 void *stream) {
+    if (!seqlens || !block_table || !result) return MLA_ERR_INVALID_ARG;
+    if (batch <= 0 || block_table_stride < 1 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+    if (batch > mla::kMaxBatch) return MLA_ERR_UNSUPPORTED;
+    hipError_t e = mla::launch_check_block_table(seqlens, batch, block_table, block_table_stride,
+                                                 num_pages, (unsigned long long *)result,
+                                                 (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_check_sparse_indices(const int32_t *block_table, int block_table_stride,
+                                    int64_t num_pages, const int32_t *indices, int topk,
+                                    int batch, int s_q, uint64_t *result, void *stream) {
+    if (!block_table || !indices || !result) return MLA_ERR_INVALID_ARG;
+    if (batch <= 0 || s_q <= 0 || topk < 1 || block_table_stride < 1 || num_pages <= 0)
+        return MLA_ERR_INVALID_ARG;
+    if ((int64_t)batch * s_q > mla::kMaxBatch) return MLA_ERR_UNSUPPORTED;
+    hipError_t e = mla::launch_check_sparse(block_table, block_table_stride, num_pages, indices,
+                                            batch * s_q, s_q, topk, (unsigned long long *)result,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

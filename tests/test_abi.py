@@ -205,3 +205,23 @@ def test_host_planner_random_batches_equal_oracle():
         ref_meta, ref_sb = oracle.plan(list(seqlens), parts, oracle.plan_overhead(s_q, h_q))
         np.testing.assert_array_equal(meta, np.array(ref_meta, dtype=np.int32))
         np.testing.assert_array_equal(sb, np.array(ref_sb, dtype=np.int32))
+
+
+def test_check_argument_errors():
+    lib = load_lib()
+    bt = lib.mla_check_block_table
+    bt.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    assert bt(None, 4, FAKE, 8, 100, FAKE, None) == INVALID
+    assert bt(FAKE, 4, FAKE, 8, 100, None, None) == INVALID
+    assert bt(FAKE, 0, FAKE, 8, 100, FAKE, None) == INVALID
+    assert bt(FAKE, 4, FAKE, 0, 100, FAKE, None) == INVALID
+    assert bt(FAKE, 4, FAKE, 8, 0, FAKE, None) == INVALID
+    assert bt(FAKE, 16385, FAKE, 8, 100, FAKE, None) == UNSUPPORTED
+    sp = lib.mla_check_sparse_indices
+    sp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert sp(FAKE, 8, 100, None, 64, 2, 1, FAKE, None) == INVALID
+    assert sp(FAKE, 8, 100, FAKE, 0, 2, 1, FAKE, None) == INVALID
+    assert sp(FAKE, 8, 100, FAKE, 64, 2, 0, FAKE, None) == INVALID
+    assert sp(FAKE, 8, 100, FAKE, 64, 8192, 4, FAKE, None) == UNSUPPORTED
