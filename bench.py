@@ -138,9 +138,50 @@ class Runner:
         torch.cuda.synchronize()
         kernel = a0.elapsed_time(a1) / steps
         n_split = int(self.split_base[-1].item())
+        try:  # a reported extra: the timed step above does not depend on it
+            graph_ms = self.measure_graph(steps)
+        except Exception as exc:  # noqa: BLE001
+            print(f"[bench] {self.name}: graph replay not measured ({exc})", file=sys.stderr)
+            graph_ms = None
         return dict(ms_per_step=ms_step, wall_ms_per_step=wall_ms_step, plan_us=plan * 1e3,
                     attn_us=attn * 1e3, combine_us=comb * 1e3, attn_kernel_us=kernel * 1e3,
-                    split_slots=n_split)
+                    split_slots=n_split, graph_ms_per_step=graph_ms)
+
+    def measure_graph(self, steps):
+        """The same step (plan, attention, combine) captured once in a HIP
+        graph and replayed `steps` times between two events.  The first
+        replay's output must equal the eager step's bit for bit."""
+        torch = self.torch
+        self.step()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = self.out.clone(), self.lse.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        self.out.zero_()
+        self.lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(self.out.view(torch.int16), ref_out.view(torch.int16))
+                and torch.equal(self.lse, ref_lse)):
+            raise RuntimeError(f"graph replay differs from the eager step in {self.name}")
+        for _ in range(10):
+            g.replay()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
     def report(self, m):
         s = m["ms_per_step"] * 1e-3
@@ -150,6 +191,8 @@ class Runner:
         bound = "hbm" if self.bytes / (PEAK_HBM_GBS * 1e9) >= self.flops / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
         return dict(
             us_per_step=round(m["ms_per_step"] * 1e3, 2),
+            us_per_step_graph=(None if m["graph_ms_per_step"] is None
+                               else round(m["graph_ms_per_step"] * 1e3, 2)),
             wall_us_per_step=round(m["wall_ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
             attn_us=round(m["attn_us"], 2), combine_us=round(m["combine_us"], 2),
             attn_kernel_us=round(m["attn_kernel_us"], 2),
