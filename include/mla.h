@@ -99,7 +99,9 @@ int mla_default_num_parts(int device, int s_q, int h_q);
  * c = mla_plan_overhead(s_q, h_q) units then one unit per page, total T.
  * With P = min(num_parts, T), the page at cost position x goes to part
  * floor(x * P / T).
- *   seqlens    int32 [batch] (device)
+ *   seqlens    int32 [batch] (device); lengths >= 0 with T < 2^31 (the
+ *              plan counts cost units in int32; the lengths are device data,
+ *              so this is the caller's contract, as are the table contents)
  *   meta       int32 [num_parts][8] (device, written): for a part with pages
  *              {b_first, j_first, b_last, j_last, split_first, 0, 0, 0} --
  *              it runs from page j_first of request b_first to page j_last of
@@ -193,7 +195,9 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
  * MLA_ERR_UNSUPPORTED).  Entries at or past the first negative one are
  * never dereferenced.
  *   kv_format 0 = bf16 cache, 1 = FP8 records; q, out, lse as for decode.
- *   batch * s_q <= 16384; topk >= 1; num_parts as for mla_get_metadata
+ *   batch * s_q <= 16384; topk >= 1 and batch * s_q * 64 * ceil(topk / 64)
+ *   < 2^31 (list positions are counted in int32; the size query returns 0
+ *   beyond it); num_parts as for mla_get_metadata
  *   (mla_default_num_parts(device, 1, h_q) suits).
  *   workspace >= mla_sparse_workspace_bytes(...) bytes, 256-byte aligned.
  */

@@ -190,7 +190,9 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
         return MLA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     unsigned char *ws = (unsigned char *)workspace;
-    const int pages_per = (topk + mla::kPage - 1) / mla::kPage;
+    const int pages_per = (int)(((int64_t)topk + mla::kPage - 1) / mla::kPage);
+    // the plan and the id lists count list positions in int32
+    if ((int64_t)rows * pages_per * mla::kPage > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
     // token ids are int32: page * 64 + slot must stay below 2^31
     if (num_pages > 0x7FFFFFFFLL / mla::kPage) return MLA_ERR_UNSUPPORTED;
     int32_t *lens = (int32_t *)(ws + L.lens), *ids = (int32_t *)(ws + L.ids);
@@ -338,6 +340,9 @@ size_t mla_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int kv_
                                   int num_parts) {
     if (batch <= 0 || s_q <= 0 || h_q <= 0 || topk <= 0 || num_parts <= 0) return 0;
     if (kv_format != 0 && kv_format != 1) return 0;
+    if ((int64_t)batch * s_q * (((int64_t)topk + mla::kPage - 1) / mla::kPage) * mla::kPage >
+        0x7FFFFFFFLL)
+        return 0;  // beyond what mla_decode_sparse accepts
     return sparse_layout(batch, s_q, h_q, topk, kv_format, num_parts).total;
 }
 

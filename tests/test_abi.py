@@ -159,6 +159,9 @@ def test_sparse_decode_argument_errors():
     assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE
     # token ids are int32: page * 64 + slot must stay below 2^31
     assert call(pages=(2**31 - 1) // 64 + 1) == UNSUPPORTED
+    # list positions are counted in int32: 16384 lists x 2^17 + 64 positions do not fit
+    assert call(batch=16384, topk=2**17 + 1, ws_bytes=2**62) == UNSUPPORTED
+    assert sz(16384, 1, 128, 2**17 + 1, 1, 64) == 0 and sz(16384, 1, 128, 2**17 - 64, 1, 64) > 0
 
 
 def _host_plan(lib, seqlens, s_q, h_q, parts):
