@@ -292,7 +292,7 @@ def sweep(steps, warmup):
 def sparse_bench(steps, warmup):
     """Sparse decode over the FP8 workload's cache (64 requests x 16384
     tokens, h_q 128, s_q 1): each query token attends to 2048 distinct listed
-    tokens.  The whole call (prep, gather, plan, decode, combine) between two
+    tokens.  The whole call (token ids, plan, decode, combine) between two
     events, launches back to back; FLOPs = 2 * h_q * (576 + 512) per listed
     token and row; bytes = the listed records read once, plus q, out, lse and
     the lists."""

@@ -262,33 +262,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         break;
                     }
                     // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for its row;
-                    // their tile scales sit at byte 512 of each record.  One tile's 16
-                    // scales are read while the previous tile's are applied, the order
-                    // pinned by fences, so the LDS latency is paid about once.
-                    auto tile_scales = [&](int k, float (&sc)[16]) {
+                    // a token's four tile scales are the 16 bytes at byte 512 of its record,
+                    // read with one 16-byte load.  Register group g (i = 4 g .. 4 g + 3) is
+                    // scaled while group g + 1's scales are read, the order pinned by fences,
+                    // so the LDS latency is paid about once.  Per score:
+                    // x = RoPE + s0 t0 + s1 t1 + s2 t2 + s3 t3, one fma at a time in that order.
+                    auto group_scales = [&](int g, f32x4 (&sc)[4]) {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            sc[i] = *(const __attribute__((address_space(3))) float *)(
-                                S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt + 4 * k);
+                        for (int r = 0; r < 4; ++r)
+                            sc[r] = *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * g + 4 * h + r) + kFp8ScalesAt);
                     };
-                    float x[16], scA[16], scB[16];
-                    __builtin_amdgcn_sched_barrier(0);
-                    tile_scales(0, scA);
-                    __builtin_amdgcn_sched_barrier(0);
-                    tile_scales(1, scB);
+                    float x[16];
+                    auto apply = [&](int g, const f32x4 (&sc)[4]) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) x[i] = acc[4][i] + scA[i] * acc[0][i];
+                        for (int r = 0; r < 4; ++r) {
+                            const int i = 4 * g + r;
+                            float v = __builtin_fmaf(sc[r][0], acc[0][i], acc[4][i]);
+                            v = __builtin_fmaf(sc[r][1], acc[1][i], v);
+                            v = __builtin_fmaf(sc[r][2], acc[2][i], v);
+                            x[i] = __builtin_fmaf(sc[r][3], acc[3][i], v);
+                        }
+                    };
+                    f32x4 scA[4], scB[4];
                     __builtin_amdgcn_sched_barrier(0);
-                    tile_scales(2, scA);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) x[i] += scB[i] * acc[1][i];
+                    group_scales(0, scA);
                     __builtin_amdgcn_sched_barrier(0);
-                    tile_scales(3, scB);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) x[i] += scA[i] * acc[2][i];
+                    group_scales(1, scB);
+                    apply(0, scA);
                     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) x[i] += scB[i] * acc[3][i];
+                    group_scales(2, scA);
+                    apply(1, scB);
+                    __builtin_amdgcn_sched_barrier(0);
+                    group_scales(3, scB);
+                    apply(2, scA);
+                    __builtin_amdgcn_sched_barrier(0);
+                    apply(3, scB);
                     __builtin_amdgcn_sched_barrier(0);
                     const int tok0 = sg.j0 * kPage + t * kHalf;
                     if (tok0 + kHalf > n_visible_all) {  // the causal edge or the segment's end
