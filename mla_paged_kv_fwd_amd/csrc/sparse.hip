@@ -20,16 +20,28 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 
+constexpr int kPerThread = 8;  // list entries each thread loads before using any
+
 // Length of list r: the position of its first negative entry, else topk.
-// All kPrepThreads threads; the result in every thread.
+// All kPrepThreads threads; the result in every thread.  Every thread loads
+// its kPerThread entries of a chunk at once (no early exit), so a chunk of
+// kPrepThreads * kPerThread entries costs one memory round trip.
 __device__ __forceinline__ int list_length(const int32_t *list, int topk, int *scratch) {
     const int tid = threadIdx.x;
     int n = topk;
-    for (int p = tid; p < topk; p += kPrepThreads)
-        if (list[p] < 0) {
-            n = p;
-            break;
+    for (int p0 = 0; p0 < topk; p0 += kPrepThreads * kPerThread) {
+        int v[kPerThread];
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int p = p0 + k * kPrepThreads + tid;
+            v[k] = p < topk ? list[p] : 0;
         }
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int p = p0 + k * kPrepThreads + tid;
+            if (v[k] < 0) n = min(n, p);
+        }
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) n = min(n, __shfl_xor(n, m));
     if ((tid & 63) == 0) scratch[tid >> 6] = n;
@@ -42,6 +54,8 @@ __device__ __forceinline__ int list_length(const int32_t *list, int topk, int *s
 
 // One work-group per pseudo-request r = b * s_q + i: lens[r] = n and
 // ids[r][p] = the cache token id of entry p for p < n, 0 for n <= p < tok_per.
+// Per chunk, the list entries are loaded first, then their block-table
+// entries, then the ids are stored: two dependent round trips per chunk.
 __global__ __launch_bounds__(kPrepThreads) void sparse_ids_kernel(
     const int32_t *__restrict__ indices, const int32_t *__restrict__ block_table,
     int64_t bt_stride, int s_q, int topk, int tok_per, int32_t *__restrict__ lens,
@@ -53,13 +67,20 @@ __global__ __launch_bounds__(kPrepThreads) void sparse_ids_kernel(
     if (tid == 0) lens[r] = n;
     const int32_t *bt = block_table + (int64_t)(r / s_q) * bt_stride;
     int32_t *dst = ids + (int64_t)r * tok_per;
-    for (int p = tid; p < tok_per; p += kPrepThreads) {
-        int id = 0;
-        if (p < n) {
-            const int pos = list[p];
-            id = bt[pos / kPage] * kPage + pos % kPage;
+    for (int p0 = 0; p0 < tok_per; p0 += kPrepThreads * kPerThread) {
+        int pos[kPerThread], page[kPerThread];
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int p = p0 + k * kPrepThreads + tid;
+            pos[k] = p < n ? list[p] : -1;
         }
-        dst[p] = id;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) page[k] = pos[k] >= 0 ? bt[pos[k] / kPage] : 0;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int p = p0 + k * kPrepThreads + tid;
+            if (p < tok_per) dst[p] = pos[k] >= 0 ? page[k] * kPage + pos[k] % kPage : 0;
+        }
     }
 }
 
