@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep", action="store_true",
                    help="only run the shape sweep (one JSON line per shape)")
+    p.add_argument("--sweep-fp8", action="store_true",
+                   help="only run the shape sweep over FP8 caches")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain 1 GiB device copies (to scale HBM counters)")
     return p.parse_args()
@@ -100,7 +102,7 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"libmla call failed in {self.name}")
 
-    def measure(self, steps, warmup):
+    def measure(self, steps, warmup, graph=True):
         """Times `steps` whole steps between two events (nothing else inside
         the timed region); then, in a second pass of `steps` steps, the plan,
         attention and combine calls separately with events on the same
@@ -138,11 +140,12 @@ class Runner:
         torch.cuda.synchronize()
         kernel = a0.elapsed_time(a1) / steps
         n_split = int(self.split_base[-1].item())
-        try:  # a reported extra: the timed step above does not depend on it
-            graph_ms = self.measure_graph(steps)
-        except Exception as exc:  # noqa: BLE001
-            print(f"[bench] {self.name}: graph replay not measured ({exc})", file=sys.stderr)
-            graph_ms = None
+        graph_ms = None
+        if graph:
+            try:  # a reported extra: the timed step above does not depend on it
+                graph_ms = self.measure_graph(steps)
+            except Exception as exc:  # noqa: BLE001
+                print(f"[bench] {self.name}: graph replay not measured ({exc})", file=sys.stderr)
         return dict(ms_per_step=ms_step, wall_ms_per_step=wall_ms_step, plan_us=plan * 1e3,
                     attn_us=attn * 1e3, combine_us=comb * 1e3, attn_kernel_us=kernel * 1e3,
                     split_slots=n_split, graph_ms_per_step=graph_ms)
@@ -257,9 +260,9 @@ SWEEP_HQ = (16, 32, 64, 128)
 SWEEP_SQ = (1, 2, 4)
 
 
-def sweep(steps, warmup):
+def sweep(steps, warmup, fp8=False):
     """Shape sweep over batch x sequence length x h_q x s_q (causal when
-    s_q > 1), bf16 cache, every request at the same length.  One JSON line per
+    s_q > 1), bf16 or FP8 cache, every request at the same length.  One JSON line per
     shape: the whole step and the attention kernel back to back, with their
     throughput and the kernel's fraction of its roofline."""
     import math
@@ -272,14 +275,14 @@ def sweep(steps, warmup):
             for h_q in SWEEP_HQ:
                 for s_q in SWEEP_SQ:
                     sl = np.full(batch, length, dtype=np.int32)
-                    q, kc, bt, slt = W.make_device_inputs(sl, s_q, h_q, False, seed=batch + length + h_q)
+                    q, kc, bt, slt = W.make_device_inputs(sl, s_q, h_q, fp8, seed=batch + length + h_q)
                     r = Runner(f"sweep b{batch} L{length} h{h_q} s{s_q}",
-                               (q, kc, bt, slt, s_q, h_q, s_q > 1, 1.0 / math.sqrt(W.D_QK), False))
-                    rep = r.report(r.measure(steps, warmup))
+                               (q, kc, bt, slt, s_q, h_q, s_q > 1, 1.0 / math.sqrt(W.D_QK), fp8))
+                    rep = r.report(r.measure(steps, warmup, graph=False))
                     a = rep["attn_kernel_us"] * 1e-6
                     frac = max(rep["alg_bytes"] / a / (PEAK_HBM_GBS * 1e9),
                                rep["alg_flops"] / a / (PEAK_BF16_TFLOPS * 1e12))
-                    print(json.dumps(dict(batch=batch, seqlen=length, h_q=h_q, s_q=s_q,
+                    print(json.dumps(dict(batch=batch, seqlen=length, h_q=h_q, s_q=s_q, fp8=fp8,
                                           step_us=rep["us_per_step"],
                                           attn_kernel_us=rep["attn_kernel_us"],
                                           attn_gbs=rep["attn_gbs"], attn_tflops=rep["attn_tflops"],
@@ -493,8 +496,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
         return
-    if args.sweep:
-        sweep(args.steps, args.warmup)
+    if args.sweep or args.sweep_fp8:
+        sweep(args.steps, args.warmup, fp8=args.sweep_fp8)
         return
     main_r = Runner(args.workload)
     m = main_r.measure(args.steps, args.warmup)
