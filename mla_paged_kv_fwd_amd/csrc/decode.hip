@@ -84,13 +84,15 @@ __device__ __forceinline__ void dequant_slice(const lds_u8 *f8, lds_u8 *bf, int 
     for (int k = 0; k < 8; ++k) {
         const int c = lg + 4 * k;  // fp8 chunk (16 codes of latent dims 16c .. 16c+15)
         const u32x4 codes = *(const u32x4 __attribute__((address_space(3))) *)(f8 + (c * 16 + lr) * 16);
+        // two codes -> two bf16 per instruction (scale 1: exact), low byte
+        // pair first, so each packed word keeps the codes' order
         unsigned packed[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes[q], false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes[q], true);
-            packed[2 * q] = (unsigned)f32_to_bf16_bits(lo[0]) | ((unsigned)f32_to_bf16_bits(lo[1]) << 16);
-            packed[2 * q + 1] = (unsigned)f32_to_bf16_bits(hi[0]) | ((unsigned)f32_to_bf16_bits(hi[1]) << 16);
+            packed[2 * q] = __builtin_bit_cast(
+                unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], 1.0f, false));
+            packed[2 * q + 1] = __builtin_bit_cast(
+                unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], 1.0f, true));
         }
         *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(2 * c, lr) * 16) =
             (u32x4){packed[0], packed[1], packed[2], packed[3]};
