@@ -108,7 +108,8 @@ __device__ __forceinline__ void dequant_slice(const lds_u8 *f8, lds_u8 *bf, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         tsc[i] = *(const f32x4 __attribute__((address_space(3))) *)(f8 + (32 * 16 + 4 * lg + i) * 16);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // No wait here: the bf16 slice is read back only by this wave, whose LDS
+    // operations execute in order, so its reads see these writes.
 }
 
 constexpr float kRescaleLog2 = 8.f;
