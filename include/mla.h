@@ -42,7 +42,17 @@
  *     KV head; d_qk 576, d_v 512, page 64.  Others: MLA_ERR_UNSUPPORTED.
  *   - Argument errors that the host can see are reported before any HIP call.
  *     Device-resident contents (page ids inside [0, num_pages), lengths that
- *     fit the block table) are the caller's contract and are not checked.
+ *     fit the block table, sparse list entries) are the caller's contract and
+ *     are not checked by the decode calls; mla_check_block_table and
+ *     mla_check_sparse_indices (end of this header) check them on demand.
+ *   - Every device call only launches kernels (no memsets, copies or
+ *     allocations), so a decode step can be captured in a HIP graph.
+ *
+ * Entry points: planning (mla_get_metadata, mla_get_metadata_host), decode
+ * (mla_decode_fwd, mla_decode_fwd_fp8, and its halves mla_decode_attn and
+ * mla_decode_combine), sparse decode over token lists (mla_decode_sparse),
+ * the cache writer (mla_kv_cache_write, mla_kv_cache_write_fp8), device-side
+ * input checks, and size / default queries.
  */
 #ifndef MLA_H
 #define MLA_H
