@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
-    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,sparse,fp8_accuracy",
+    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,sparse,sparse16,fp8_accuracy",
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -292,10 +292,10 @@ def sweep(steps, warmup, fp8=False):
                     torch.cuda.empty_cache()
 
 
-def sparse_bench(steps, warmup):
+def sparse_bench(steps, warmup, h_q=128):
     """Sparse decode over the FP8 workload's cache (64 requests x 16384
-    tokens, h_q 128, s_q 1): each query token attends to 2048 distinct listed
-    tokens.  The whole call (token ids, plan, decode, combine) between two
+    tokens, s_q 1; h_q 128, or the first h_q heads of its queries): each query
+    token attends to 2048 distinct listed tokens.  The whole call (token ids, plan, decode, combine) between two
     events, launches back to back; FLOPs = 2 * h_q * (576 + 512) per listed
     token and row; bytes = the listed records read once, plus q, out, lse and
     the lists."""
@@ -305,7 +305,8 @@ def sparse_bench(steps, warmup):
     import mla_paged_kv_fwd_amd as mla
     import workloads as W
 
-    q, kc, bt, sl, s_q, h_q, _, scale, _ = W.make_config_device("fp8")
+    q, kc, bt, sl, s_q, h_all, _, scale, _ = W.make_config_device("fp8")
+    q = q[:, :, :h_q].contiguous()
     batch, length, topk = q.shape[0], int(sl[0].item()), 2048
     g = torch.Generator(device="cuda")
     g.manual_seed(79)
@@ -506,9 +507,11 @@ def main():
     workloads = {args.workload: rep}
     del main_r
     for name in [x for x in args.extra.split(",") if x]:
-        if name in ("kvwrite", "fp8_accuracy", "sparse"):
+        if name in ("kvwrite", "fp8_accuracy", "sparse", "sparse16"):
             rep_x = (kv_write_bench(args.steps, args.warmup) if name == "kvwrite" else
-                     sparse_bench(args.steps, args.warmup) if name == "sparse" else fp8_accuracy())
+                     sparse_bench(args.steps, args.warmup) if name == "sparse" else
+                     sparse_bench(args.steps, args.warmup, h_q=16) if name == "sparse16" else
+                     fp8_accuracy())
             print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
             workloads[name] = rep_x
             torch.cuda.empty_cache()
