@@ -77,7 +77,9 @@ typedef enum {
 #define MLA_PAGE 64
 #define MLA_FP8_RECORD 656
 #define MLA_META_INTS 8
-#define MLA_MAX_BATCH 32768
+/* Largest batch (requests; for mla_decode_sparse: batch * s_q lists) and
+ * largest num_parts any call accepts; beyond them MLA_ERR_UNSUPPORTED. */
+#define MLA_MAX_BATCH 16384
 #define MLA_MAX_PARTS 16384
 
 /* Static string for a status code.  Thread-safe; never NULL. */

@@ -153,11 +153,31 @@ def _validate(q, kcache, block_table, seqlens, fp8):
         raise MlaError("block_table must be int32 [batch, width]")
     if seqlens is not None and (seqlens.dtype != torch.int32 or seqlens.dim() != 1):
         raise MlaError("seqlens must be int32 [batch]")
+    # the kernels index seqlens and block_table rows by q's batch index, and
+    # size out and the workspace from q
+    if block_table.shape[0] != q.shape[0]:
+        raise MlaError("block_table must have one row per request of q")
+    if seqlens is not None and seqlens.shape[0] != q.shape[0]:
+        raise MlaError("seqlens must have one entry per request of q")
     for t in (q, kcache, block_table, seqlens):
         if t is None:
             continue
         if not t.is_cuda or not t.is_contiguous():
             raise MlaError("all tensors must be contiguous CUDA tensors")
+
+
+def _check_plan(q, meta, split_base, num_parts):
+    """A caller's plan must have the shapes the kernels index: meta
+    [num_parts, 8] and split_base [batch + 1], int32, on q's device."""
+    if meta is None and split_base is None:
+        return
+    if meta is None or split_base is None or num_parts is None:
+        raise MlaError("pass meta, split_base and num_parts together")
+    for t, shape, name in ((meta, (int(num_parts), META_INTS), "meta"),
+                           (split_base, (q.shape[0] + 1,), "split_base")):
+        if (t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_cuda
+                or t.device != q.device or not t.is_contiguous()):
+            raise MlaError(f"{name} must be a contiguous int32 CUDA tensor {list(shape)} on q's device")
 
 
 def _outputs(q, out, lse):
@@ -177,11 +197,17 @@ def _outputs(q, out, lse):
     return out, lse
 
 
-def _workspace(q, num_parts, workspace):
-    b, s_q, h_q, _ = q.shape
-    need = workspace_bytes(b, s_q, h_q, num_parts)
+def _workspace(q, num_parts, workspace, need=None):
+    if need is None:
+        b, s_q, h_q, _ = q.shape
+        need = workspace_bytes(b, s_q, h_q, num_parts)
     if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+        return torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    if (workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda
+            or workspace.device != q.device or not workspace.is_contiguous()):
+        raise MlaError("workspace must be a contiguous 1-D uint8 CUDA tensor on q's device")
+    if workspace.numel() < need:
+        raise MlaError(f"workspace holds {workspace.numel()} bytes; {need} needed")
     return workspace
 
 
@@ -189,6 +215,8 @@ def decode_attn(q, kcache, block_table, seqlens, softmax_scale, causal, meta, sp
                 num_parts, workspace, out=None, lse=None, fp8=False):
     """Attention kernel only (the first half of decode)."""
     _validate(q, kcache, block_table, seqlens, fp8)
+    _check_plan(q, meta, split_base, num_parts)
+    workspace = _workspace(q, num_parts, workspace)
     out, lse = _outputs(q, out, lse)
     b, s_q, h_q, _ = q.shape
     _check(lib().mla_decode_attn(
@@ -201,7 +229,18 @@ def decode_attn(q, kcache, block_table, seqlens, softmax_scale, causal, meta, sp
 
 def decode_combine(split_base, num_parts, workspace, out, lse):
     """LSE merge of split partials (the second half of decode)."""
+    if out.dtype != torch.bfloat16 or out.dim() != 4 or out.shape[-1] != D_V:
+        raise MlaError("out must be bf16 [batch, s_q, h_q, 512]")
     b, s_q, h_q, _ = out.shape
+    if not out.is_cuda or not out.is_contiguous():
+        raise MlaError("out must be a contiguous CUDA tensor")
+    if (lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (b, s_q, h_q)
+            or lse.device != out.device or not lse.is_contiguous()):
+        raise MlaError("lse must be a contiguous fp32 CUDA tensor [batch, s_q, h_q] on out's device")
+    if (split_base.dtype != torch.int32 or tuple(split_base.shape) != (b + 1,)
+            or split_base.device != out.device or not split_base.is_contiguous()):
+        raise MlaError("split_base must be a contiguous int32 CUDA tensor [batch + 1] on out's device")
+    workspace = _workspace(out, num_parts, workspace, workspace_bytes(b, s_q, h_q, num_parts))
     _check(lib().mla_decode_combine(_ptr(split_base), b, s_q, h_q, num_parts, _ptr(workspace),
                                     workspace.numel(), _ptr(out), _ptr(lse), _stream()),
            "mla_decode_combine")
@@ -263,8 +302,9 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
         _raise_if_bad(check_block_table(block_table, seqlens, kcache.shape[0]),
                       "block table / seqlens")
     b, s_q, h_q, _ = q.shape
-    if meta is None:
+    if meta is None and split_base is None:
         meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts)
+    _check_plan(q, meta, split_base, num_parts)
     out, lse = _outputs(q, out, lse)
     workspace = _workspace(q, num_parts, workspace)
     fn = lib().mla_decode_fwd_fp8 if fp8 else lib().mla_decode_fwd
@@ -294,6 +334,8 @@ def kv_cache_write(k_new, block_table, seqlens, kcache, fp8=False):
         if not t.is_cuda or not t.is_contiguous():
             raise MlaError("all tensors must be contiguous CUDA tensors")
     batch, n_new = k_new.shape[0], k_new.shape[1]
+    if block_table.shape[0] != batch or seqlens.shape[0] != batch:
+        raise MlaError("block_table and seqlens must have one row / entry per request of k_new")
     if _checks_enabled():
         _raise_if_bad(check_block_table(block_table, seqlens, kcache.shape[0]),
                       "block table / seqlens")
@@ -327,8 +369,9 @@ def decode_sparse(q, kcache, block_table, indices, softmax_scale, fp8=False, num
     if num_parts is None:
         num_parts = default_num_parts(1, h_q, q.device.index)
     need = sparse_workspace_bytes(b, s_q, h_q, topk, num_parts, fp8)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    if need == 0:
+        raise MlaError("sparse decode: lists too long for int32 positions")
+    workspace = _workspace(q, num_parts, workspace, need)
     out, lse = _outputs(q, out, lse)
     _check(lib().mla_decode_sparse(
         _ptr(q), _ptr(kcache), 1 if fp8 else 0, kcache.shape[0], _ptr(block_table),

@@ -31,7 +31,8 @@ hipError_t launch_combine(const int32_t *split_base, int batch, int M, const flo
 }  // namespace mla
 
 static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::kPage &&
-                  MLA_FP8_RECORD == mla::kTokBytesFp8 && MLA_META_INTS == mla::kMetaInts,
+                  MLA_FP8_RECORD == mla::kTokBytesFp8 && MLA_META_INTS == mla::kMetaInts &&
+                  MLA_MAX_BATCH == mla::kMaxBatch && MLA_MAX_PARTS == mla::kMaxParts,
               "header and kernels disagree");
 
 namespace {

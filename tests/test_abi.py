@@ -228,3 +228,37 @@ def test_check_argument_errors():
     assert sp(FAKE, 8, 100, FAKE, 0, 2, 1, FAKE, None) == INVALID
     assert sp(FAKE, 8, 100, FAKE, 64, 2, 0, FAKE, None) == INVALID
     assert sp(FAKE, 8, 100, FAKE, 64, 8192, 4, FAKE, None) == UNSUPPORTED
+
+
+def _header_macro(name):
+    m = re.search(r"#define\s+%s\s+(\d+)" % name, open(HEADER).read())
+    assert m, name
+    return int(m.group(1))
+
+
+def test_header_limits_match_the_library():
+    """MLA_MAX_BATCH and MLA_MAX_PARTS are the limits the calls enforce: at
+    the limit the call gets past the size checks (the host planner succeeds;
+    the decode call then stops at the workspace check, which comes after
+    them), one past it the call returns MLA_ERR_UNSUPPORTED."""
+    lib = load_lib()
+    max_batch, max_parts = _header_macro("MLA_MAX_BATCH"), _header_macro("MLA_MAX_PARTS")
+    fn = lib.mla_get_metadata_host
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+
+    def host_plan(batch, parts):
+        sl = np.full(batch, 100, dtype=np.int32)
+        meta = np.zeros((parts, 8), dtype=np.int32)
+        sb = np.zeros(batch + 1, dtype=np.int32)
+        return fn(sl.ctypes.data, batch, 1, 16, parts, meta.ctypes.data, sb.ctypes.data)
+
+    assert host_plan(max_batch, 64) == OK
+    assert host_plan(max_batch + 1, 64) == UNSUPPORTED
+    assert host_plan(7, max_parts) == OK
+    assert host_plan(7, max_parts + 1) == UNSUPPORTED
+    # decode: past the size checks means the workspace check answers
+    assert _decode(lib, batch=max_batch, ws_bytes=256) == WORKSPACE
+    assert _decode(lib, batch=max_batch + 1, ws_bytes=256) == UNSUPPORTED
+    assert _decode(lib, parts=max_parts, ws_bytes=256) == WORKSPACE
+    assert _decode(lib, parts=max_parts + 1, ws_bytes=256) == UNSUPPORTED

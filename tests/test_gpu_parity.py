@@ -91,8 +91,10 @@ def test_growing_scores_match_oracle(seqlens, s_q, h_q, causal, num_parts, fp8):
 
 WIDE = [
     # seqlens, s_q, h_q, causal, fp8: query rows scaled by their own power of
-    # two and a quarter of their entries made 2^12 smaller (the FP8 kernels
-    # split each query row into two E4M3 halves under a per-row scale)
+    # two and a quarter of their entries made 2^12 smaller, so scores span a
+    # wide range and small query entries must keep their weight (a path that
+    # rounded q to a narrow format, or accumulated the scores in lower
+    # precision, would fail here)
     ([5, 64, 257, 700], 1, 128, False, True),
     ([2, 66, 130, 400], 2, 64, True, True),
     ([300, 64], 1, 16, False, True),
