@@ -22,7 +22,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+# MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP per clock x 2.4 GHz
+PEAK_BF16_TFLOPS = 2517.0
+FLUSH_BYTES = 1 << 30        # written before each flushed iteration (> the 256 MB MALL)
 METRIC = "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), h_q=16 and h_q=128"
 
 
@@ -32,8 +34,13 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="membound")
-    p.add_argument("--extra", default="computebound,fp8,longctx,kvwrite,sparse,sparse16,fp8_accuracy",
+    p.add_argument("--extra",
+                   default="computebound,fp8,longctx,tiny,kvwrite,sparse,sparse16,fp8_accuracy,ceilings",
                    help="comma list of further workloads to measure ('' for none)")
+    p.add_argument("--flush", action="store_true",
+                   help="every workload also reports steps timed one by one after a 1 GiB "
+                        "cache-evicting write (membound, tiny and sparse always do)")
+    p.add_argument("--flush-iters", type=int, default=30)
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep", action="store_true",
@@ -131,6 +138,8 @@ class Runner:
         plan = np.mean([e[0].elapsed_time(e[1]) for e in evs])
         attn = np.mean([e[1].elapsed_time(e[2]) for e in evs])
         comb = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+        pct_step = percentiles([e[0].elapsed_time(e[3]) * 1e3 for e in evs])
+        pct_attn = percentiles([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(stream)
         for _ in range(steps):
@@ -148,7 +157,28 @@ class Runner:
                 print(f"[bench] {self.name}: graph replay not measured ({exc})", file=sys.stderr)
         return dict(ms_per_step=ms_step, wall_ms_per_step=wall_ms_step, plan_us=plan * 1e3,
                     attn_us=attn * 1e3, combine_us=comb * 1e3, attn_kernel_us=kernel * 1e3,
-                    split_slots=n_split, graph_ms_per_step=graph_ms)
+                    split_slots=n_split, graph_ms_per_step=graph_ms,
+                    step_us_pct=pct_step, attn_us_pct=pct_attn)
+
+    def measure_flushed(self, iters):
+        """`iters` steps timed one by one, each after writing FLUSH_BYTES to a
+        scratch buffer (evicting the 256 MB MALL and the L2s), with events
+        around the whole step and around the attention call: p10 / median /
+        p90 in microseconds."""
+        torch = self.torch
+        flush = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device=self.q.device)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+        for k in range(iters):
+            flush.fill_(k & 0xFF)
+            self.step(evs[k])
+        torch.cuda.synchronize()
+        res = dict(iters=iters, flush_bytes=FLUSH_BYTES,
+                   step_us=percentiles([e[0].elapsed_time(e[3]) * 1e3 for e in evs]),
+                   attn_us=percentiles([e[1].elapsed_time(e[2]) * 1e3 for e in evs]))
+        res["gbs_median"] = round(self.bytes / res["step_us"]["p50"] / 1e3, 1)
+        res["tflops_median"] = round(self.flops / res["step_us"]["p50"] / 1e6, 1)
+        del flush
+        return res
 
     def measure_graph(self, steps):
         """The same step (plan, attention, combine) captured once in a HIP
@@ -199,6 +229,7 @@ class Runner:
             wall_us_per_step=round(m["wall_ms_per_step"] * 1e3, 2), plan_us=round(m["plan_us"], 2),
             attn_us=round(m["attn_us"], 2), combine_us=round(m["combine_us"], 2),
             attn_kernel_us=round(m["attn_kernel_us"], 2),
+            step_us_pct=m["step_us_pct"], attn_us_pct=m["attn_us_pct"],
             split_slots=m["split_slots"], num_parts=self.num_parts,
             alg_bytes=self.bytes, alg_flops=self.flops,
             gbs=round(gbs, 1), tflops=round(tfl, 1),
@@ -206,6 +237,77 @@ class Runner:
             hbm_frac=round(gbs / PEAK_HBM_GBS, 4), mfma_frac=round(tfl / PEAK_BF16_TFLOPS, 4),
             bound=bound,
             roofline_frac=round(max(gbs / PEAK_HBM_GBS, tfl / PEAK_BF16_TFLOPS), 4))
+
+
+def percentiles(xs):
+    """p10, median and p90 of a list of times (microseconds)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "p50": round(float(np.median(a)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def ceilings(steps):
+    """Measured ceilings of the part, in the same run as the decode legs: a
+    plain streaming read of 2 GiB (16-byte loads, several grid sizes, the
+    best kept) and back-to-back bf16 MFMA loops (16x16x32 and 32x32x16, one
+    or two waves per SIMD, the best kept).  Launches timed back to back
+    between two events, after three untimed ones."""
+    import ctypes
+
+    import torch
+    import mla_paged_kv_fwd_amd as mla
+
+    lib = ctypes.CDLL(mla.CEILING_LIB_PATH)
+    lib.mla_ceiling_blocks.argtypes = [ctypes.c_int]
+    lib.mla_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.mla_ceiling_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.mla_ceiling_mfma_flops.restype = ctypes.c_double
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def timed(launch, n):
+        for _ in range(3):
+            if launch() != 0:
+                raise RuntimeError("ceiling launch failed")
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(n):
+            launch()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / n * 1e-3  # seconds per launch
+
+    nbytes = 2 << 30
+    buf = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    read = {}
+    for bpc in (2, 4, 8, 16):
+        sink = torch.empty((lib.mla_ceiling_blocks(bpc) * 256,), dtype=torch.int32, device="cuda")
+        t = timed(lambda: lib.mla_ceiling_stream_read(buf.data_ptr(), nbytes, bpc,
+                                                      sink.data_ptr(), s), max(steps, 10))
+        read[f"{bpc}_per_cu"] = round(nbytes / t / 1e9, 1)
+    del buf
+    mfma = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        for bpc in (1, 2):
+            iters = 20000
+            sink = torch.empty((lib.mla_ceiling_blocks(bpc) * 256,), dtype=torch.float32,
+                               device="cuda")
+            t = timed(lambda: lib.mla_ceiling_mfma(shape, iters, bpc, sink.data_ptr(), s),
+                      max(steps // 2, 5))
+            mfma[f"{name}_{bpc}_wave_per_simd"] = round(
+                lib.mla_ceiling_mfma_flops(shape, iters, bpc) / t / 1e12, 1)
+    best_read = max(read.values())
+    best_16 = max(v for k, v in mfma.items() if k.startswith("16x16x32"))
+    best_32 = max(v for k, v in mfma.items() if k.startswith("32x32x16"))
+    torch.cuda.empty_cache()
+    return dict(hbm_read_gbs=best_read, hbm_read_frac=round(best_read / PEAK_HBM_GBS, 4),
+                mfma_16x16x32_tflops=best_16, mfma_32x32x16_tflops=best_32,
+                mfma_frac=round(max(best_16, best_32) / PEAK_BF16_TFLOPS, 4),
+                read_by_grid=read, mfma_by_shape=mfma)
 
 
 def kv_write_bench(steps, warmup):
@@ -292,7 +394,7 @@ def sweep(steps, warmup, fp8=False):
                     torch.cuda.empty_cache()
 
 
-def sparse_bench(steps, warmup, h_q=128):
+def sparse_bench(steps, warmup, h_q=128, flush_iters=30):
     """Sparse decode over the FP8 workload's cache (64 requests x 16384
     tokens, s_q 1; h_q 128, or the first h_q heads of its queries): each query
     token attends to 2048 distinct listed tokens.  The whole call (token ids, plan, decode, combine) between two
@@ -332,11 +434,26 @@ def sparse_bench(steps, warmup, h_q=128):
     a1.record(stream)
     torch.cuda.synchronize()
     us = a0.elapsed_time(a1) / steps * 1e3
+    # the same call timed one by one after a cache-evicting write: the listed
+    # records (86 MB) would otherwise stay in the 256 MB MALL between calls
+    flush = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(flush_iters)]
+    for k, (f0, f1) in enumerate(evs):
+        flush.fill_(k & 0xFF)
+        f0.record(stream)
+        lib.mla_decode_sparse(*args)
+        f1.record(stream)
+    torch.cuda.synchronize()
+    flushed = percentiles([f0.elapsed_time(f1) * 1e3 for f0, f1 in evs])
+    del flush
     rows = batch * s_q
     flops = 2 * h_q * (W.D_QK + W.D_V) * topk * rows
     alg = rows * topk * (W.FP8_RECORD + 4) + rows * h_q * (2 * W.D_QK + 2 * W.D_V + 4)
     res = dict(shape=f"batch {batch} x {length}, s_q {s_q}, h_q {h_q}, fp8 cache, {topk} listed tokens",
-               us=round(us, 2), alg_flops=flops, alg_bytes=alg, tflops=round(flops / us / 1e6, 1),
+               us=round(us, 2), us_flushed=flushed, alg_flops=flops, alg_bytes=alg,
+               tflops=round(flops / us / 1e6, 1),
+               tflops_flushed_median=round(flops / flushed["p50"] / 1e6, 1),
                mfma_frac=round(flops / us / 1e6 / PEAK_BF16_TFLOPS, 4),
                gbs=round(alg / us / 1e3, 1))
     del q, kc, bt, sl, idx, ws, out, lse
@@ -456,9 +573,10 @@ def cpu_baseline(name, seconds):
                 tflops=round(f / dt / 1e12, 6), seconds=round(dt, 3))
 
 
-def roofline(rep, workload):
+def roofline(rep, workload, ceil=None):
     """Roofline object for the dominant kernel of the workload's step: the
-    attention kernel, timed with events on the stream it runs on."""
+    attention kernel, timed with events on the stream it runs on.  With the
+    ceilings leg measured, also its fraction of the part's measured rate."""
     import workloads as W
 
     cfg = W.CONFIGS[workload]
@@ -472,8 +590,14 @@ def roofline(rep, workload):
         achieved, peak, unit = rep["attn_gbs"], PEAK_HBM_GBS, "GB/s"
     else:
         achieved, peak, unit = rep["attn_tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"
-    return {"bound": rep["bound"], "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+    res = {"bound": rep["bound"], "achieved": achieved, "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+    if ceil:
+        measured = (ceil["hbm_read_gbs"] if rep["bound"] == "hbm" else
+                    max(ceil["mfma_16x16x32_tflops"], ceil["mfma_32x32x16_tflops"]))
+        res["peak_measured"] = measured
+        res["frac_of_measured"] = round(achieved / measured, 4)
+    return res
 
 
 def main():
@@ -500,17 +624,23 @@ def main():
     if args.sweep or args.sweep_fp8:
         sweep(args.steps, args.warmup, fp8=args.sweep_fp8)
         return
+    always_flushed = ("membound", "tiny")
     main_r = Runner(args.workload)
     m = main_r.measure(args.steps, args.warmup)
     rep = main_r.report(m)
+    if args.flush or args.workload in always_flushed:
+        rep["flushed"] = main_r.measure_flushed(args.flush_iters)
     print(f"[bench] {args.workload}: {json.dumps(rep)}", file=sys.stderr, flush=True)
     workloads = {args.workload: rep}
     del main_r
     for name in [x for x in args.extra.split(",") if x]:
-        if name in ("kvwrite", "fp8_accuracy", "sparse", "sparse16"):
+        if name in ("kvwrite", "fp8_accuracy", "sparse", "sparse16", "ceilings"):
             rep_x = (kv_write_bench(args.steps, args.warmup) if name == "kvwrite" else
-                     sparse_bench(args.steps, args.warmup) if name == "sparse" else
-                     sparse_bench(args.steps, args.warmup, h_q=16) if name == "sparse16" else
+                     sparse_bench(args.steps, args.warmup, flush_iters=args.flush_iters)
+                     if name == "sparse" else
+                     sparse_bench(args.steps, args.warmup, h_q=16, flush_iters=args.flush_iters)
+                     if name == "sparse16" else
+                     ceilings(args.steps) if name == "ceilings" else
                      fp8_accuracy())
             print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
             workloads[name] = rep_x
@@ -518,10 +648,25 @@ def main():
             continue
         r = Runner(name)
         rep_x = r.report(r.measure(args.steps, args.warmup))
+        if args.flush or name in always_flushed:
+            rep_x["flushed"] = r.measure_flushed(args.flush_iters)
+        if name == "tiny":  # a latency figure: the whole step and its calls, in microseconds
+            rep_x = {k: rep_x[k] for k in ("us_per_step", "plan_us", "attn_us", "combine_us",
+                                           "attn_kernel_us", "step_us_pct", "flushed",
+                                           "alg_bytes", "alg_flops")}
+            rep_x["bound"] = "latency"
         print(f"[bench] {name}: {json.dumps(rep_x)}", file=sys.stderr, flush=True)
         workloads[name] = rep_x
         del r
         torch.cuda.empty_cache()
+    ceil = workloads.get("ceilings")
+    if ceil:  # every throughput workload's kernel also against the measured ceilings
+        for name, r in workloads.items():
+            if isinstance(r, dict) and "attn_gbs" in r:
+                r["attn_frac_of_measured"] = round(max(
+                    r["attn_gbs"] / ceil["hbm_read_gbs"],
+                    r["attn_tflops"] / max(ceil["mfma_16x16x32_tflops"],
+                                           ceil["mfma_32x32x16_tflops"])), 4)
     head = workloads[args.workload]
     attn_gbs = head["attn_gbs"]
     line = {
@@ -541,7 +686,7 @@ def main():
                    "batch": int(len(W.CONFIGS[args.workload]['seqlens'])) if not isinstance(
                        W.CONFIGS[args.workload]['seqlens'], tuple) else 64,
                    "parallelism": "single GPU"},
-        "roofline": roofline(head, args.workload),
+        "roofline": roofline(head, args.workload, ceil),
         "workloads": workloads,
     }
     if args.cpu_baseline:

@@ -26,6 +26,8 @@ META_INTS = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
+# measured ceilings of the part (include/mla_ceiling.h); loaded by bench.py only
+CEILING_LIB_PATH = os.path.join(_HERE, "libmla_ceiling.so")
 _lib = None
 
 _P = ctypes.c_void_p

@@ -262,3 +262,20 @@ def test_header_limits_match_the_library():
     assert _decode(lib, batch=max_batch + 1, ws_bytes=256) == UNSUPPORTED
     assert _decode(lib, parts=max_parts, ws_bytes=256) == WORKSPACE
     assert _decode(lib, parts=max_parts + 1, ws_bytes=256) == UNSUPPORTED
+
+
+def test_ceiling_library_exports_its_header():
+    """The ceilings library (bench.py's measured rates) exports every call
+    include/mla_ceiling.h declares, and refuses bad arguments before any
+    launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "mla_paged_kv_fwd_amd", "libmla_ceiling.so"))
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mla_ceiling.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(mla_ceiling_[a-z0-9_]+)\s*\(", text)))
+    assert len(names) == 4
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.mla_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.mla_ceiling_stream_read(None, 1024, 4, FAKE, None) == -1
+    assert lib.mla_ceiling_mfma(2, 10, 1, FAKE, None) == -1
