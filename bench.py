@@ -69,7 +69,7 @@ class Runner:
         self.batch = seqlens.shape[0]
         self.bytes = W.algorithmic_bytes(seqlens, self.s_q, self.h_q, self.fp8)
         self.flops = W.algorithmic_flops(seqlens, self.s_q, self.h_q, self.causal)
-        self.num_parts = mla.default_num_parts(self.s_q, self.h_q)
+        self.num_parts = mla.default_num_parts(self.s_q, self.h_q, fp8=self.fp8)
         dev = self.q.device
         self.meta = torch.empty((self.num_parts, mla.META_INTS), dtype=torch.int32, device=dev)
         self.split_base = torch.empty((self.batch + 1,), dtype=torch.int32, device=dev)
@@ -414,7 +414,7 @@ def sparse_bench(steps, warmup, h_q=128, flush_iters=30):
     g.manual_seed(79)
     idx = torch.argsort(torch.rand((batch, s_q, length), generator=g, device="cuda"), dim=-1)[
         ..., :topk].to(torch.int32).contiguous()
-    num_parts = mla.default_num_parts(1, h_q)
+    num_parts = mla.default_num_parts(1, h_q, fp8=True, sparse=True)
     ws = torch.empty((mla.sparse_workspace_bytes(batch, s_q, h_q, topk, num_parts, fp8=True),),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((batch, s_q, h_q, W.D_V), dtype=torch.bfloat16, device="cuda")
@@ -581,8 +581,10 @@ def roofline(rep, workload, ceil=None):
 
     cfg = W.CONFIGS[workload]
     rows = cfg["s_q"] * cfg["h_q"]
-    if rows < 64:
+    if rows < 32:
         kernel = "decode_rowgroup_kernel<%s>" % ("true" if cfg["fp8"] else "false")
+    elif rows == 128 and not cfg["fp8"]:
+        kernel = "decode_rows128_kernel"
     else:
         kernel = "decode_rows64_fp8_kernel<false>" if cfg["fp8"] else "decode_rows64_kernel<false>"
     traffic = measured_traffic(kernel, workload)

@@ -98,8 +98,15 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
 int mla_plan_overhead(int s_q, int h_q);
 
 /* Plan size suited to the kernels on `device` (a multiple of 8 derived from
- * the CU count); < 0 on error (status code).  Needs a visible GPU. */
+ * the CU count: one work-group per CU); < 0 on error (status code).  Needs a
+ * visible GPU.  mla_default_num_parts is for the bf16 dense decode;
+ * mla_default_num_parts_ex gives the size for a cache format (kv_format 0 =
+ * bf16, 1 = FP8 records) and for sparse decode (sparse = 1; s_q is then
+ * ignored: the plan covers one-token problems), whose kernels may run a part
+ * on a different number of work-groups.  Any num_parts gives the same result;
+ * these sizes fill the GPU in one round. */
 int mla_default_num_parts(int device, int s_q, int h_q);
+int mla_default_num_parts_ex(int device, int s_q, int h_q, int kv_format, int sparse);
 
 /*
  * Split-KV plan.  Cuts the batch's pages into num_parts contiguous pieces of
@@ -210,7 +217,7 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
  *   batch * s_q <= 16384; topk >= 1 and batch * s_q * 64 * ceil(topk / 64)
  *   < 2^31 (list positions are counted in int32; the size query returns 0
  *   beyond it); num_parts as for mla_get_metadata
- *   (mla_default_num_parts(device, 1, h_q) suits).
+ *   (mla_default_num_parts_ex(device, 1, h_q, kv_format, 1) suits).
  *   workspace >= mla_sparse_workspace_bytes(...) bytes, 256-byte aligned.
  */
 size_t mla_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int kv_format,

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "mla_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "mla_plan_overhead": (_I, [_I, _I]),
     "mla_default_num_parts": (_I, [_I, _I, _I]),
+    "mla_default_num_parts_ex": (_I, [_I, _I, _I, _I, _I]),
     "mla_get_metadata": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "mla_get_metadata_host": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "mla_decode_fwd": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
@@ -105,23 +106,26 @@ def workspace_bytes(batch, s_q, h_q, num_parts):
     return lib().mla_workspace_bytes(batch, s_q, h_q, num_parts)
 
 
-def default_num_parts(s_q, h_q, device=None):
+def default_num_parts(s_q, h_q, device=None, fp8=False, sparse=False):
+    """Plan size that fills the GPU in one round for this shape and cache
+    format (sparse=True: sparse decode of h_q heads)."""
     dev = torch.cuda.current_device() if device is None else int(device)
-    n = lib().mla_default_num_parts(dev, s_q, h_q)
+    n = lib().mla_default_num_parts_ex(dev, s_q, h_q, 1 if fp8 else 0, 1 if sparse else 0)
     if n < 0:
         _check(n, "mla_default_num_parts")
     return n
 
 
-def get_metadata(seqlens, s_q, h_q, num_parts=None):
-    """Plan split-KV work on the GPU.  seqlens: int32 CUDA tensor [batch].
+def get_metadata(seqlens, s_q, h_q, num_parts=None, fp8=False):
+    """Plan split-KV work on the GPU.  seqlens: int32 CUDA tensor [batch];
+    without num_parts, the size that suits the cache format (fp8).
 
     Returns (meta int32 [num_parts, 8], split_base int32 [batch + 1], num_parts).
     """
     if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
         raise MlaError("seqlens must be a contiguous int32 CUDA tensor")
     if num_parts is None:
-        num_parts = default_num_parts(s_q, h_q, seqlens.device.index)
+        num_parts = default_num_parts(s_q, h_q, seqlens.device.index, fp8=fp8)
     batch = seqlens.shape[0]
     meta = torch.empty((num_parts, META_INTS), dtype=torch.int32, device=seqlens.device)
     split_base = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
@@ -305,7 +309,7 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
                       "block table / seqlens")
     b, s_q, h_q, _ = q.shape
     if meta is None and split_base is None:
-        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts)
+        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts, fp8=fp8)
     _check_plan(q, meta, split_base, num_parts)
     out, lse = _outputs(q, out, lse)
     workspace = _workspace(q, num_parts, workspace)
@@ -369,7 +373,7 @@ def decode_sparse(q, kcache, block_table, indices, softmax_scale, fp8=False, num
         _raise_if_bad(check_sparse_indices(block_table, indices, kcache.shape[0]), "sparse lists")
     topk = indices.shape[2]
     if num_parts is None:
-        num_parts = default_num_parts(1, h_q, q.device.index)
+        num_parts = default_num_parts(1, h_q, q.device.index, fp8=fp8, sparse=True)
     need = sparse_workspace_bytes(b, s_q, h_q, topk, num_parts, fp8)
     if need == 0:
         raise MlaError("sparse decode: lists too long for int32 positions")

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["api.hip", "plan.hip", "decode.hip", "decode_rows64.hip", "decode_rows64_fp8.hip",
-           "combine.hip", "kv_write.hip", "sparse.hip", "check.hip"]
+           "decode_rows128.hip", "combine.hip", "kv_write.hip", "sparse.hip", "check.hip"]
 # measured ceilings of the part (stream read, MFMA loops), a library of its own
 CEILING_LIB = os.path.join(HERE, "libmla_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]

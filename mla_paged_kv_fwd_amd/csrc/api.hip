@@ -14,6 +14,7 @@ hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 int decode_rows_per_group();
 hipError_t launch_decode_rows64(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_rows64_fp8(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_rows128(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_kv_write(const uint16_t *k_new, int batch, int n_new, const int32_t *block_table,
                            int64_t bt_stride, const int32_t *seqlens, void *cache, bool fp8,
                            hipStream_t stream);
@@ -37,12 +38,25 @@ static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::k
 
 namespace {
 
-// Kernel choice: 64 query rows per work-group with specialised score / value
-// waves when a request has at least 32 rows (32 rows leave half the group as
-// padding: the problem is memory-bound and reads each page once instead of
-// twice); 16 rows per work-group otherwise.
+// Kernel choice: 128 query rows per work-group for 128-row requests over a
+// bf16 cache (dense decode); 64 query rows per work-group with specialised
+// score / value waves when a request has at least 32 rows (32 rows leave half
+// the group as padding: the problem is memory-bound and reads each page once
+// instead of twice); 16 rows per work-group otherwise.  With 256 or 512 rows
+// the 64-row kernel is as fast or faster (a part's row groups share its
+// half-pages through L2, and with half the parts per CU fewer requests are
+// split, so fewer partial results are written and merged).
+bool use_rows128(int M, int kv_format, int token_list) {
+    return M == 128 && kv_format == 0 && !token_list;
+}
 bool use_rows64(int M) { return M >= 32; }
 int rows64_groups(int M) { return (M + 63) / 64; }  // M = 32 pads one group
+// work-groups per part of the kernel a call runs on
+int groups_per_part(int M, int kv_format, int token_list) {
+    if (use_rows128(M, kv_format, token_list)) return M / 128;
+    if (use_rows64(M) || token_list) return rows64_groups(M);
+    return M / 16;
+}
 
 bool shape_supported(int s_q, int h_q) {
     return (s_q == 1 || s_q == 2 || s_q == 4) && (h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128);
@@ -104,7 +118,10 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.token_list = token_list;
     hipError_t e;
     // token lists always run on the 64-row kernels (M = 16 pads one group)
-    if (use_rows64(M) || token_list) {
+    if (use_rows128(M, kv_format, token_list)) {
+        a.row_groups = M / 128;
+        e = mla::launch_decode_rows128(a, (hipStream_t)stream);
+    } else if (use_rows64(M) || token_list) {
         a.row_groups = rows64_groups(M);
         e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
                            : mla::launch_decode_rows64(a, (hipStream_t)stream);
@@ -243,8 +260,9 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts) {
 
 int mla_plan_overhead(int s_q, int h_q) { return mla::plan_overhead(s_q, h_q); }
 
-int mla_default_num_parts(int device, int s_q, int h_q) {
+int mla_default_num_parts_ex(int device, int s_q, int h_q, int kv_format, int sparse) {
     if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+    if ((kv_format != 0 && kv_format != 1) || (sparse != 0 && sparse != 1)) return MLA_ERR_INVALID_ARG;
     if (device < 0 || device >= 64) return MLA_ERR_INVALID_ARG;
     if (g_cu_count[device] <= 0) {
         int cus = 0;
@@ -253,13 +271,18 @@ int mla_default_num_parts(int device, int s_q, int h_q) {
             return MLA_ERR_HIP;
         g_cu_count[device] = cus;
     }
-    // one work-group per CU, all in one round: a part spans M / 64
-    // work-groups in the 64-row kernel and M / 16 in the 16-row kernel
-    const int M = s_q * h_q;
+    // one work-group per CU, all in one round: a part spans as many
+    // work-groups as the kernel that runs it has row groups (sparse decode
+    // plans one-token problems of h_q rows)
+    const int M = sparse ? h_q : s_q * h_q;
     int parts = g_cu_count[device];
-    parts = parts / (use_rows64(M) ? rows64_groups(M) : M / mla::decode_rows_per_group());
+    parts = parts / groups_per_part(M, kv_format, sparse);
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
+}
+
+int mla_default_num_parts(int device, int s_q, int h_q) {
+    return mla_default_num_parts_ex(device, s_q, h_q, 0, 0);
 }
 
 mla_status mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,

@@ -58,7 +58,7 @@ def test_decode_step_replays_in_a_graph(h_q, fp8):
                        poison=True)
     q, kc, bt, sl = to_device(case)
     batch = len(seqlens)
-    parts = mla.default_num_parts(s_q, h_q)
+    parts = mla.default_num_parts(s_q, h_q, fp8=fp8)
     meta = torch.empty((parts, mla.META_INTS), dtype=torch.int32, device="cuda")
     sb = torch.empty((batch + 1,), dtype=torch.int32, device="cuda")
     ws = torch.empty((mla.workspace_bytes(batch, s_q, h_q, parts),), dtype=torch.uint8,
@@ -94,7 +94,7 @@ def test_sparse_call_replays_in_a_graph(h_q, fp8):
             idx[b, i, :n] = rng.choice(L, n, replace=False)
     q, kc, bt, _ = to_device(case)
     idx_d = torch.from_numpy(idx).cuda()
-    parts = mla.default_num_parts(1, h_q)
+    parts = mla.default_num_parts(1, h_q, fp8=fp8, sparse=True)
     ws = torch.empty((mla.sparse_workspace_bytes(len(seqlens), s_q, h_q, topk, parts, fp8=fp8),),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((len(seqlens), s_q, h_q, W.D_V), dtype=torch.bfloat16, device="cuda")

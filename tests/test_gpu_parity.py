@@ -198,3 +198,25 @@ def test_full_size_workloads_on_sampled_rows(name):
     compare(out[b, i, h], lse[b, i, h], ref_out, ref_lse, name)
     # a property over every row: all outputs finite
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+ROWS128 = [
+    # seqlens, s_q, h_q, causal, num_parts: lengths on both sides of the
+    # 16-token unit and 32-token step boundaries of the 128-row kernel, parts
+    # that walk many requests, and four row groups (M = 512)
+    ([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 95, 96, 97, 1000, 2500], 1, 128, False, 3),
+    ([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 95, 96, 97, 1000, 2500], 1, 128, False, 37),
+    ([2, 17, 33, 250, 1200], 2, 64, True, 5),
+    ([4, 18, 34, 251, 900], 4, 128, True, 6),
+    ([4, 18, 34, 251, 900], 4, 32, False, 64),
+]
+
+
+@pytest.mark.parametrize("seqlens,s_q,h_q,causal,num_parts", ROWS128)
+def test_128_row_groups_match_oracle(seqlens, s_q, h_q, causal, num_parts):
+    case = W.make_case(seqlens, s_q, h_q, seed=300 + h_q + s_q, causal=causal, spare_pages=2,
+                       poison=True)
+    out, lse = run_gpu(case, num_parts=num_parts)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse,
+            f"128-row {seqlens} s_q={s_q} h_q={h_q} causal={causal} parts={num_parts}")
