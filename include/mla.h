@@ -32,7 +32,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every device
  *     call only enqueues work on it and returns; nothing synchronises.
  *   - The caller owns every buffer.  The library allocates and frees nothing
- *     and keeps no state besides a per-device cache of the CU count.
+ *     and keeps no state besides a per-device cache of the CU count (and the
+ *     fixed scratch array of mla_decode_fwd_noalloc, with its per-device
+ *     address).
  *   - Tensors are dense and row-major:
  *       q     bf16  [batch][s_q][h_q][576]
  *       out   bf16  [batch][s_q][h_q][512]
@@ -50,7 +52,8 @@
  *
  * Entry points: planning (mla_get_metadata, mla_get_metadata_host), decode
  * (mla_decode_fwd, mla_decode_fwd_fp8, and its halves mla_decode_attn and
- * mla_decode_combine), sparse decode over token lists (mla_decode_sparse),
+ * mla_decode_combine; mla_decode_fwd_noalloc, which allocates nothing and
+ * needs no workspace), sparse decode over token lists (mla_decode_sparse),
  * the cache writer (mla_kv_cache_write, mla_kv_cache_write_fp8), device-side
  * input checks, and size / default queries.
  */
@@ -193,6 +196,31 @@ mla_status mla_decode_attn(const void *q, const void *kcache, int kv_format, int
 mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int h_q,
                               int num_parts, const void *workspace, size_t workspace_bytes,
                               void *out, float *lse, void *stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): mla_decode_fwd / mla_decode_fwd_fp8 (kv_format 0 / 1) with the
+ * plan made inside the call (mla_default_num_parts_ex parts) and the plan and
+ * the split workspace held in the library's own scratch, a fixed device array
+ * of MLA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends.  The call allocates and frees nothing;
+ * the caller passes inputs and outputs as for mla_decode_fwd.  Problems whose
+ * plan and workspace need more than the scratch (mla_noalloc_scratch_need
+ * returns the need on the current device, 0 for bad arguments) get
+ * MLA_ERR_WORKSPACE before any launch.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (different streams,
+ * or threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs clearing between calls (every value read is written by the
+ * same call).  Three kernels on `stream` (plan, attention, merge).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+size_t mla_noalloc_scratch_need(int batch, int s_q, int h_q, int kv_format);
+mla_status mla_decode_fwd_noalloc(const void *q, const void *kcache, int kv_format,
+                                  int64_t num_pages, const int32_t *block_table,
+                                  int block_table_stride, const int32_t *seqlens, int batch,
+                                  int s_q, int h_q, float softmax_scale, int causal, void *out,
+                                  float *lse, void *stream);
 
 /*
  * Sparse decode: query token i of request b attends only to the cached tokens

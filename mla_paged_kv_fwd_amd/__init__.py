@@ -14,7 +14,7 @@ __all__ = [
     "MlaError", "lib", "D_QK", "D_V", "PAGE", "FP8_RECORD", "META_INTS",
     "default_num_parts", "plan_overhead", "workspace_bytes", "get_metadata",
     "get_metadata_host", "decode", "decode_attn", "decode_combine", "decode_sparse",
-    "sparse_workspace_bytes", "kv_cache_write",
+    "sparse_workspace_bytes", "kv_cache_write", "decode_noalloc", "noalloc_scratch_need",
     "status_string",
 ]
 
@@ -58,6 +58,8 @@ _SIGNATURES = {
                                _P, _P]),
     "mla_kv_cache_write_fp8": (_I, [_P, _I, _I, _P, _I, _P, _P, _I64, _P]),
     "mla_check_block_table": (_I, [_P, _I, _P, _I, _I64, _P, _P]),
+    "mla_noalloc_scratch_need": (_SZ, [_I, _I, _I, _I]),
+    "mla_decode_fwd_noalloc": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _P]),
     "mla_check_sparse_indices": (_I, [_P, _I, _I64, _P, _I, _I, _I, _P, _P]),
 }
 
@@ -318,6 +320,28 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
               _ptr(seqlens), b, s_q, h_q, float(softmax_scale), int(bool(causal)), _ptr(meta),
               _ptr(split_base), num_parts, _ptr(workspace), workspace.numel(), _ptr(out),
               _ptr(lse), _stream()), "mla_decode_fwd")
+    return out, lse
+
+
+def noalloc_scratch_need(batch, s_q, h_q, fp8=False):
+    """Scratch bytes decode_noalloc needs for this problem on the current
+    device (it accepts up to MLA_NOALLOC_SCRATCH_BYTES, 128 MiB)."""
+    return lib().mla_noalloc_scratch_need(batch, s_q, h_q, 1 if fp8 else 0)
+
+
+def decode_noalloc(q, kcache, block_table, seqlens, softmax_scale, causal, out=None, lse=None,
+                   fp8=False):
+    """decode() through the allocation-free entry point: the library plans and
+    keeps the plan and the split partials in its own fixed scratch, so the
+    call allocates nothing (pass out and lse to allocate nothing here
+    either).  Calls that overlap on one GPU race on that scratch."""
+    _validate(q, kcache, block_table, seqlens, fp8)
+    out, lse = _outputs(q, out, lse)
+    b, s_q, h_q, _ = q.shape
+    _check(lib().mla_decode_fwd_noalloc(
+        _ptr(q), _ptr(kcache), 1 if fp8 else 0, kcache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seqlens), b, s_q, h_q, float(softmax_scale), int(bool(causal)),
+        _ptr(out), _ptr(lse), _stream()), "mla_decode_fwd_noalloc")
     return out, lse
 
 

@@ -2,6 +2,8 @@
 // reported before the first HIP call.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/mla.h"
 #include "common.h"
 
@@ -29,6 +31,11 @@ hipError_t launch_check_sparse(const int32_t *block_table, int64_t bt_stride, in
                                unsigned long long *result, hipStream_t stream);
 hipError_t launch_combine(const int32_t *split_base, int batch, int M, const float *o_part,
                           const float *lse_part, uint16_t *out, float *lse, hipStream_t stream);
+}  // namespace mla
+
+namespace mla {
+// Scratch of the allocation-free decode (see scratch_address below).
+__device__ __align__(256) unsigned char scratch[(size_t)MLA_NOALLOC_SCRATCH_BYTES];
 }  // namespace mla
 
 static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::kPage &&
@@ -234,6 +241,30 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
 
 int g_cu_count[64];
 
+// Scratch of the allocation-free decode (mla_decode_fwd_noalloc): the plan and
+// the split workspace of one call, in a file-scope device array that every
+// GPU the library runs on holds until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kNoallocScratch = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+std::atomic<unsigned char *> g_scratch_dev[64];
+
+mla_status scratch_address(unsigned char **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MLA_ERR_HIP;
+    unsigned char *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(mla::scratch)) != hipSuccess || !addr)
+            return MLA_ERR_HIP;
+        p = (unsigned char *)addr;
+        g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,7 +274,9 @@ const char *mla_status_string(int status) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARG: return "invalid argument";
     case MLA_ERR_UNSUPPORTED: return "unsupported shape";
-    case MLA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MLA_ERR_WORKSPACE:
+        return "workspace missing, too small or misaligned (or, for the allocation-free "
+               "decode, the problem needs more than its fixed scratch)";
     case MLA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
     }
@@ -358,6 +391,53 @@ mla_status mla_decode_fwd_fp8(const void *q, const void *kcache_fp8, int64_t num
     return decode_fwd(q, kcache_fp8, 1, num_pages, block_table, block_table_stride, seqlens, batch,
                       s_q, h_q, softmax_scale, causal, meta, split_base, num_parts, workspace,
                       workspace_bytes_, out, lse, stream);
+}
+
+size_t mla_noalloc_scratch_need(int batch, int s_q, int h_q, int kv_format) {
+    if (batch <= 0 || s_q <= 0 || h_q <= 0 || (kv_format != 0 && kv_format != 1)) return 0;
+    if (!shape_supported(s_q, h_q) || batch > mla::kMaxBatch) return 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const int parts = mla_default_num_parts_ex(dev, s_q, h_q, kv_format, 0);
+    if (parts <= 0) return 0;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up((size_t)parts * mla::kMetaInts * 4) + up(((size_t)batch + 1) * 4) +
+           workspace_bytes(batch, s_q, h_q, parts);
+}
+
+mla_status mla_decode_fwd_noalloc(const void *q, const void *kcache, int kv_format,
+                                  int64_t num_pages, const int32_t *block_table,
+                                  int block_table_stride, const int32_t *seqlens, int batch,
+                                  int s_q, int h_q, float softmax_scale, int causal, void *out,
+                                  float *lse, void *stream) {
+    // host-visible argument errors first, as for the other decode calls
+    if (!q || !kcache || !block_table || !seqlens || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (kv_format != 0 && kv_format != 1) return MLA_ERR_INVALID_ARG;
+    if (num_pages <= 0 || block_table_stride < 1) return MLA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+    if (batch <= 0 || s_q <= 0 || h_q <= 0) return MLA_ERR_INVALID_ARG;
+    if (batch > mla::kMaxBatch || !shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    const int parts = mla_default_num_parts_ex(dev, s_q, h_q, kv_format, 0);
+    if (parts <= 0) return parts < 0 ? (mla_status)parts : MLA_ERR_HIP;
+    // scratch layout: meta, split_base, then the split workspace (256-byte aligned)
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t meta_off = 0, sb_off = up((size_t)parts * mla::kMetaInts * 4);
+    const size_t ws_off = sb_off + up(((size_t)batch + 1) * 4);
+    const size_t ws_bytes = workspace_bytes(batch, s_q, h_q, parts);
+    if (ws_off + ws_bytes > kNoallocScratch) return MLA_ERR_WORKSPACE;
+    unsigned char *base = nullptr;
+    mla_status st = scratch_address(&base);
+    if (st != MLA_OK) return st;
+    int32_t *meta = (int32_t *)(base + meta_off), *split_base = (int32_t *)(base + sb_off);
+    hipError_t e = mla::launch_plan(seqlens, batch, mla::plan_overhead(s_q, h_q), parts, meta,
+                                    split_base, (hipStream_t)stream);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    return decode_fwd(q, kcache, kv_format, num_pages, block_table, block_table_stride, seqlens,
+                      batch, s_q, h_q, softmax_scale, causal, meta, split_base, parts,
+                      base + ws_off, ws_bytes, out, lse, stream);
 }
 
 size_t mla_sparse_workspace_bytes(int batch, int s_q, int h_q, int topk, int kv_format,
