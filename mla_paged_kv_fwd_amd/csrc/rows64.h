@@ -144,17 +144,20 @@ __device__ __forceinline__ void stage_output(float *X, const f32x16 (&o)[2][8], 
 
 // Zeroes the accumulators with MFMAs (0 x 0 + 0), so they are born in the
 // accumulator registers; plain zero stores get hoisted into 256 VGPRs of
-// constants by the compiler.
+// constants by the compiler.  Each tile gets its own zero operand from an asm
+// statement: identical MFMAs would be merged into one whose result is then
+// copied into the other tiles.
 __device__ __forceinline__ void zero_acc(f32x16 (&o)[2][8]) {
-    u32x4 zw;
-    asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
-                 : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
-    const bf16x8 zf = __builtin_bit_cast(bf16x8, zw);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 8; ++dt) {
+            u32x4 zw;
+            asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                         : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
+            const bf16x8 zf = __builtin_bit_cast(bf16x8, zw);
             o[r][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, (f32x16){}, 0, 0, 0);
+        }
 }
 
 }  // namespace rows64
