@@ -462,45 +462,50 @@ def sparse_bench(steps, warmup, h_q=128, flush_iters=30):
 
 
 def fp8_accuracy():
-    """FP8 cache against bf16 cache on the same latent: the FP8 workload's
-    shape (64 requests x 16384 tokens, s_q 1, h_q 128), N(0,1) rows rounded to
-    bf16, written once as bf16 rows and once as FP8 records by the cache
-    writer; both decoded with the same queries.  Reports how far the FP8
-    result moves from the bf16 one (a property of the format and its
-    quantiser, not a parity check)."""
+    """FP8 cache against bf16 cache on the same latent, across shapes: h_q in
+    {16, 64, 128} x L in {4096, 16384, 65536}, s_q 1, 2^20 cached tokens per
+    shape (batch = 2^20 / L; h_q 128 at L 16384 is the FP8 workload's shape).
+    N(0,1) rows rounded to bf16 are written once as bf16 rows and once as FP8
+    records by the cache writer and both are decoded with the same queries.
+    Reports how far the FP8 result moves from the bf16 one: a property of the
+    format and its quantiser, not a parity check (the GPU tests set this shift
+    beside the oracle's own on sampled rows)."""
     import math
 
     import torch
     import mla_paged_kv_fwd_amd as mla
     import workloads as W
 
-    batch, length, h_q = 64, 16384, 128
-    g = torch.Generator(device="cuda")
-    g.manual_seed(78)
-    pages = length // W.PAGE
-    bt = torch.randperm(batch * pages, generator=g, device="cuda").to(torch.int32).reshape(
-        batch, pages).contiguous()
-    sl = torch.full((batch,), length, dtype=torch.int32, device="cuda")
-    rows = torch.randn((batch, length, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
-    q = torch.randn((batch, 1, h_q, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
-    kc16 = torch.empty((batch * pages, W.PAGE, W.D_QK), dtype=torch.bfloat16, device="cuda")
-    kc8 = torch.empty((batch * pages, W.PAGE, W.FP8_RECORD), dtype=torch.uint8, device="cuda")
-    mla.kv_cache_write(rows, bt, sl, kc16)
-    mla.kv_cache_write(rows, bt, sl, kc8, fp8=True)
-    del rows
-    scale = 1.0 / math.sqrt(W.D_QK)
-    o16, l16 = mla.decode(q, kc16, bt, sl, scale, False)
-    o8, l8 = mla.decode(q, kc8, bt, sl, scale, False, fp8=True)
-    torch.cuda.synchronize()
-    d = o8.float() - o16.float()
-    rel = (d.norm() / o16.float().norm()).item()
-    res = dict(shape=f"batch {batch} x {length}, s_q 1, h_q {h_q}",
-               out_max_abs=round(d.abs().max().item(), 6), out_rel_l2=round(rel, 6),
-               out_ref_max_abs=round(o16.float().abs().max().item(), 6),
-               lse_max_abs=round((l8 - l16).abs().max().item(), 6),
-               lse_mean_abs=round((l8 - l16).abs().mean().item(), 6))
-    del kc16, kc8
-    torch.cuda.empty_cache()
+    res = []
+    for h_q in (16, 64, 128):
+        for length in (4096, 16384, 65536):
+            batch = (1 << 20) // length
+            g = torch.Generator(device="cuda")
+            g.manual_seed(78 + h_q + length)
+            pages = length // W.PAGE
+            bt = torch.randperm(batch * pages, generator=g, device="cuda").to(torch.int32).reshape(
+                batch, pages).contiguous()
+            sl = torch.full((batch,), length, dtype=torch.int32, device="cuda")
+            rows = torch.randn((batch, length, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
+            q = torch.randn((batch, 1, h_q, W.D_QK), generator=g, device="cuda").to(torch.bfloat16)
+            kc16 = torch.empty((batch * pages, W.PAGE, W.D_QK), dtype=torch.bfloat16, device="cuda")
+            kc8 = torch.empty((batch * pages, W.PAGE, W.FP8_RECORD), dtype=torch.uint8, device="cuda")
+            mla.kv_cache_write(rows, bt, sl, kc16)
+            mla.kv_cache_write(rows, bt, sl, kc8, fp8=True)
+            del rows
+            scale = 1.0 / math.sqrt(W.D_QK)
+            o16, l16 = mla.decode(q, kc16, bt, sl, scale, False)
+            o8, l8 = mla.decode(q, kc8, bt, sl, scale, False, fp8=True)
+            torch.cuda.synchronize()
+            d = o8.float() - o16.float()
+            res.append(dict(h_q=h_q, L=length, batch=batch,
+                            out_max_abs=round(d.abs().max().item(), 6),
+                            out_rel_l2=round((d.norm() / o16.float().norm()).item(), 6),
+                            out_ref_max_abs=round(o16.float().abs().max().item(), 6),
+                            lse_max_abs=round((l8 - l16).abs().max().item(), 6),
+                            lse_mean_abs=round((l8 - l16).abs().mean().item(), 6)))
+            del kc16, kc8, o16, o8, l16, l8, d
+            torch.cuda.empty_cache()
     return res
 
 
