@@ -24,8 +24,30 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP per clock x 2.4 GHz
 PEAK_BF16_TFLOPS = 2517.0
-FLUSH_BYTES = 1 << 30        # written before each flushed iteration (> the 256 MB MALL)
+FLUSH_BYTES = 1 << 30        # written, then another buffer of this size read, before each
+                             # flushed iteration (> the 256 MB MALL and the 8 x 4 MB L2s)
 METRIC = "MLA decode TFLOPS + HBM GB/s (fraction of MI355X peak), h_q=16 and h_q=128"
+
+
+class CacheEvict:
+    """Leaves the caches holding none of the workload's lines and no dirty
+    lines: FLUSH_BYTES written to one scratch buffer, then FLUSH_BYTES of
+    another read.  The read evicts the written lines, so their write-back
+    happens here and not inside the timed call that follows (a write alone
+    leaves up to the MALL's size of dirty lines, whose write-back made the
+    memory-bound step about 50% slower)."""
+
+    def __init__(self, torch, device):
+        self.torch = torch
+        self.w = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device=device)
+        self.r = torch.ones((FLUSH_BYTES // 8,), dtype=torch.int64, device=device)
+
+    def __call__(self, k):
+        self.w.fill_(k & 0xFF)
+        self.r.sum()
+
+    def free(self):
+        del self.w, self.r
 
 
 def parse():
@@ -38,8 +60,9 @@ def parse():
                    default="computebound,fp8,longctx,tiny,kvwrite,sparse,sparse16,fp8_accuracy,ceilings",
                    help="comma list of further workloads to measure ('' for none)")
     p.add_argument("--flush", action="store_true",
-                   help="every workload also reports steps timed one by one after a 1 GiB "
-                        "cache-evicting write (membound, tiny and sparse always do)")
+                   help="every workload also reports steps timed one by one after a cache "
+                        "eviction (1 GiB written, another 1 GiB read; membound, tiny and "
+                        "sparse always do)")
     p.add_argument("--flush-iters", type=int, default=30)
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -161,15 +184,15 @@ class Runner:
                     step_us_pct=pct_step, attn_us_pct=pct_attn)
 
     def measure_flushed(self, iters):
-        """`iters` steps timed one by one, each after writing FLUSH_BYTES to a
-        scratch buffer (evicting the 256 MB MALL and the L2s), with events
-        around the whole step and around the attention call: p10 / median /
-        p90 in microseconds."""
+        """`iters` steps timed one by one, each after a CacheEvict (the 256 MB
+        MALL and the L2s hold none of the workload and nothing dirty), with
+        events around the whole step and around the attention call: p10 /
+        median / p90 in microseconds."""
         torch = self.torch
-        flush = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device=self.q.device)
+        flush = CacheEvict(torch, self.q.device)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
         for k in range(iters):
-            flush.fill_(k & 0xFF)
+            flush(k)
             self.step(evs[k])
         torch.cuda.synchronize()
         res = dict(iters=iters, flush_bytes=FLUSH_BYTES,
@@ -177,7 +200,7 @@ class Runner:
                    attn_us=percentiles([e[1].elapsed_time(e[2]) * 1e3 for e in evs]))
         res["gbs_median"] = round(self.bytes / res["step_us"]["p50"] / 1e3, 1)
         res["tflops_median"] = round(self.flops / res["step_us"]["p50"] / 1e6, 1)
-        del flush
+        flush.free()
         return res
 
     def measure_graph(self, steps):
@@ -434,19 +457,19 @@ def sparse_bench(steps, warmup, h_q=128, flush_iters=30):
     a1.record(stream)
     torch.cuda.synchronize()
     us = a0.elapsed_time(a1) / steps * 1e3
-    # the same call timed one by one after a cache-evicting write: the listed
-    # records (86 MB) would otherwise stay in the 256 MB MALL between calls
-    flush = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device="cuda")
+    # the same call timed one by one after a CacheEvict: the listed records
+    # (86 MB) would otherwise stay in the 256 MB MALL between calls
+    flush = CacheEvict(torch, "cuda")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(flush_iters)]
     for k, (f0, f1) in enumerate(evs):
-        flush.fill_(k & 0xFF)
+        flush(k)
         f0.record(stream)
         lib.mla_decode_sparse(*args)
         f1.record(stream)
     torch.cuda.synchronize()
     flushed = percentiles([f0.elapsed_time(f1) * 1e3 for f0, f1 in evs])
-    del flush
+    flush.free()
     rows = batch * s_q
     flops = 2 * h_q * (W.D_QK + W.D_V) * topk * rows
     alg = rows * topk * (W.FP8_RECORD + 4) + rows * h_q * (2 * W.D_QK + 2 * W.D_V + 4)
