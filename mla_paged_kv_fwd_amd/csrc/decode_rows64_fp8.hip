@@ -11,11 +11,11 @@
 // for all 64 rows, one half-page behind, and issue all loads.
 //
 // Dequantisation happens in registers, exactly:
-//   - a K fragment (8 codes of one token) is read with ds_read_b64 and turned
-//     into bf16 with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (every E4M3FN
-//     value is a bf16 value); QK^T keeps one accumulator per 128-dim tile plus
-//     one for the RoPE dims, and the token's tile scales weight the tile
-//     accumulators afterwards, in fp32;
+//   - K fragments (16 codes of one token, two k-steps) are read with
+//     ds_read_b128 and turned into bf16 with v_cvt_scalef32_pk_bf16_fp8 at
+//     scale 1 (every E4M3FN value is a bf16 value); QK^T keeps one
+//     accumulator per 128-dim tile plus one for the RoPE dims, and the
+//     token's tile scales weight the tile accumulators afterwards, in fp32;
 //   - a V fragment (one dim of 8 tokens) comes from ds_read_b64_tr_b8; each
 //     code is widened to fp32, multiplied by its token's tile scale and
 //     rounded once to bf16 (P stays the plain bf16 softmax weight, as in the
@@ -27,9 +27,10 @@
 // A half-page (32 records, 20992 bytes) lands in LDS as the plain memory
 // image, 21 direct-to-LDS loads of 1 KB each; records past the segment's last
 // token are replaced by that token's record.  With a 656-byte record stride
-// (164 dwords, 36 mod 64 banks) both the ds_read_b64 K reads of 16 tokens and
-// the transposed V reads of 8 tokens hit distinct banks, so no swizzle is
-// needed.
+// (164 dwords, 36 mod 64 banks) both the 16-byte K reads of 16 tokens and the
+// transposed V reads of 8 tokens hit distinct banks, so no swizzle is needed.
+// (Tokens 16 apart share banks, so 8-byte K reads, served 32 lanes at a time,
+// would conflict two ways.)
 //
 // Token-list mode (sparse decode, kList): each "request" is one query token's
 // list of cache token ids; the score waves stage the ids of half-page t + 3 in
@@ -235,13 +236,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
             int n_visible = a.causal ? sg.L - (a.s_q - 1 - qi) : sg.L;
             n_visible = n_visible > 0 ? n_visible : 0;
             const int n_visible_all = a.causal ? sg.L - (a.s_q - 1) : sg.L;
-            // Q^T operand for 32x32x16: lane holds dims 16 ks + 8 h .. +8 of its row
-            // (loaded into VGPRs, then moved to the accumulator registers)
+            // Q^T operand for 32x32x16 (loaded into VGPRs, then moved to the
+            // accumulator registers).  Latent k-steps 2 pp + e (pp < 16, e < 2)
+            // give lane half h dims 32 pp + 16 h + 8 e .. +8, so that one
+            // 16-byte read of 16 codes per lane feeds both k-steps of a pair
+            // (K reads below); RoPE k-steps 32 + r give it dims 512 + 16 r + 8 h.
             bf16x8 qf[kDQk / 16];
-            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row_q) * kDQk + 8 * h;
+            const uint16_t *qrow = q + ((int64_t)sg.b * a.M + row_q) * kDQk;
             bf16x8 qv[kDQk / 16];
 #pragma unroll
-            for (int ks = 0; ks < kDQk / 16; ++ks) qv[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+            for (int ks = 0; ks < kDQk / 16; ++ks)
+                qv[ks] = *(const bf16x8 *)(qrow + (ks < kDV / 16 ? 32 * (ks >> 1) + 16 * h + 8 * (ks & 1)
+                                                                 : 16 * ks + 8 * h));
 #pragma unroll
             for (int ks = 0; ks < kDQk / 16; ++ks) asm volatile("; q to agprs" : "=a"(qf[ks]) : "0"(qv[ks]));
             // lsum: sum of the fp32 weights (for the lse); wsum: sum of the
@@ -287,14 +293,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         sc[i] = *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt);
                     // S^T (32 tokens x 32 rows) per 128-dim tile and for the RoPE dims
                     f32x16 acc[5];
-                    // K codes of k-steps 2 pp, 2 pp + 1 (8 bytes each), kPairs
-                    // pairs in flight ahead of their MFMAs; the fences pin
-                    // that order
+                    // K codes of k-steps 2 pp, 2 pp + 1: the 16 codes at dims
+                    // 32 pp + 16 h of this lane's token, one 16-byte read,
+                    // kPairs pairs in flight ahead of their MFMAs; the fences
+                    // pin that order.  A 16-lane group of the read covers 16
+                    // tokens, whose records start 36 banks apart (mod 64):
+                    // every lane of the group hits its own 4 banks.
                     constexpr int kPairs = 4;
                     auto read_pair = [&](int pp) {
-                        const u32x2 a = *(const lds_u32x2 *)(S + krec + 32 * pp + 8 * h);
-                        const u32x2 b = *(const lds_u32x2 *)(S + krec + 32 * pp + 16 + 8 * h);
-                        return (u32x4){a[0], a[1], b[0], b[1]};
+                        return *(const lds_u32x4 *)(S + krec + 32 * pp + 16 * h);
                     };
                     bf16x8 kr[4];
 #pragma unroll
