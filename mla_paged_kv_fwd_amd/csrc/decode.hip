@@ -20,6 +20,22 @@
 // then one 1 KB ds_read_b128 block per wave, and the V^T operand of PV a
 // ds_read_b64_tr_b16 (4 tokens x 16 dims transposed per 16-lane group); the
 // XOR keeps both free of bank conflicts.
+//
+// FP8 cache: the slice holds the raw 656-byte records, chunk c of token t in
+// slot c * 16 + (t ^ 8 * (c & 1)), and both operands are read straight from
+// the codes (three slices per wave in flight instead of a bf16 copy):
+//   - K: 8 codes of one token per lane (ds_read_b64), converted exactly to
+//     bf16 (every E4M3FN value is a bf16 value); the token's four tile scales
+//     weight the per-tile partial scores afterwards, in fp32;
+//   - V: one ds_read_b64_tr_b8 per pair of 16-dim tiles: the lane's 16-lane
+//     group points its rows 0..3 at the group's 4 tokens in one chunk and
+//     rows 4..7 at the same tokens in the next, so a lane gets one dim of its
+//     4 tokens for each of the two tiles: the A operands of two 16x16x16
+//     MFMAs.  The codes are converted exactly; each 128-dim tile's token
+//     scales are folded into its own bf16 copy of P.
+// The swizzle puts the two chunks of a V read on different banks (tokens 8
+// apart are 32 banks apart); the K reads of 32 lanes are 256 contiguous
+// bytes either way.
 #include <math.h>
 
 #include "common.h"
@@ -57,14 +73,20 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
         for (int s = 0; s < kLoadsBf16; ++s)
             dma16(src + s * 64, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
     } else {
-        int t = kSlice * w + lr;  // FP8 slices are not swizzled
-        t = t < tok_last ? t : tok_last;
-        const unsigned char *rec = kv + (phys * kPage + t) * kTokBytesFp8;
+        // slot (4 s + lg) * 16 + lr holds token lr ^ 8 (lg & 1) of chunk 4 s + lg
+        const unsigned char *rec[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            int t = kSlice * w + (lr ^ (8 * e));
+            t = t < tok_last ? t : tok_last;
+            rec[e] = kv + (phys * kPage + t) * kTokBytesFp8;
+        }
+        const unsigned char *mine = rec[lg & 1];
 #pragma unroll
         for (int s = 0; s < kLoadsFp8; ++s) {
             int cidx = 4 * s + lg;
             cidx = cidx < 40 ? cidx : 40;  // slots past chunk 40 are padding
-            dma16(rec + cidx * 16, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
+            dma16(mine + cidx * 16, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
         }
     }
 }
@@ -72,49 +94,24 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
 // slot of chunk c of token t in a swizzled bf16 slice
 __device__ __forceinline__ int slot16(int c, int t) { return c * 16 + (t ^ (4 * (c & 1))); }
 
-// FP8 slice (chunk-major, 41 chunks x 16 tokens) -> bf16 slice (72 x 16).
-// The latent codes are converted exactly (every E4M3FN value is a bf16
-// value); their per-128-dim scales are applied after the MFMAs instead (to
-// the per-tile partial scores, and to P for the value product), so the fp32
-// scale is never rounded into the operands.  The RoPE chunks are copied.
-// Also returns the scales of the lane's 4 tokens (4*lg + i): tsc[i][tile].
-__device__ __forceinline__ void dequant_slice(const lds_u8 *f8, lds_u8 *bf, int lane, f32x4 *tsc) {
-    const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int c = lg + 4 * k;  // fp8 chunk (16 codes of latent dims 16c .. 16c+15)
-        const u32x4 codes = *(const u32x4 __attribute__((address_space(3))) *)(f8 + (c * 16 + lr) * 16);
-        // two codes -> two bf16 per instruction (scale 1: exact), low byte
-        // pair first, so each packed word keeps the codes' order
-        unsigned packed[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            packed[2 * q] = __builtin_bit_cast(
-                unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], 1.0f, false));
-            packed[2 * q + 1] = __builtin_bit_cast(
-                unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[q], 1.0f, true));
-        }
-        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(2 * c, lr) * 16) =
-            (u32x4){packed[0], packed[1], packed[2], packed[3]};
-        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(2 * c + 1, lr) * 16) =
-            (u32x4){packed[4], packed[5], packed[6], packed[7]};
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int r = 33 + lg + 4 * k;  // RoPE chunk in the record
-        const u32x4 v = *(const u32x4 __attribute__((address_space(3))) *)(f8 + (r * 16 + lr) * 16);
-        *(u32x4 __attribute__((address_space(3))) *)(bf + slot16(64 + r - 33, lr) * 16) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        tsc[i] = *(const f32x4 __attribute__((address_space(3))) *)(f8 + (32 * 16 + 4 * lg + i) * 16);
-    // No wait here: the bf16 slice is read back only by this wave, whose LDS
-    // operations execute in order, so its reads see these writes.
+// byte address of chunk c of token t in a swizzled FP8 slice
+__device__ __forceinline__ int slot8(int c, int t) { return (c * 16 + (t ^ (8 * (c & 1)))) * 16; }
+
+// 8 E4M3FN codes (little-endian in two dwords) -> 8 bf16, exactly (scale 1).
+__device__ __forceinline__ bf16x8 codes8_to_bf16(unsigned lo, unsigned hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 constexpr float kRescaleLog2 = 8.f;
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 struct RowState {
     f32x4 o[kDV / 16];  // O^T tiles: lane holds dims 16*dt + 4*(lane/16) + i of row lane%16
@@ -148,14 +145,24 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[i] = s0[i] + s1[i];
     } else {
+        // raw records: latent k-step ks = chunk 2 ks + lg / 2 of token lr,
+        // 8 codes at byte 8 (lg & 1); RoPE k-step 16 + r = chunk 33 + 4 r + lg
+        // (8 bf16); the token scales sit in chunk 32
         f32x4 acc[5];
 #pragma unroll
         for (int t = 0; t < 5; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < kDQk / 32; ++ks) {
-            const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3))) *)(S + (ks * 64 + kl) * 16);
-            const int t = ks < 16 ? ks / 4 : 4;
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc[t], 0, 0, 0);
+        for (int ks = 0; ks < kDV / 32; ++ks) {
+            const int c = 2 * ks + (lg >> 1);
+            const u32x2_t cv =
+                *(const u32x2_t __attribute__((address_space(3))) *)(S + slot8(c, lr) + 8 * (lg & 1));
+            acc[ks / 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16(cv[0], cv[1]), qf[ks],
+                                                                  acc[ks / 4], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const bf16x8 kf = *(const bf16x8 __attribute__((address_space(3))) *)(S + slot8(33 + 4 * r + lg, lr));
+            acc[4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kDV / 32 + r], acc[4], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -213,13 +220,34 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
         st.wsum = st.wsum * alpha + add_bf16_pair(pw[1], add_bf16_pair(pw[0], 0.f));
     }
     // O^T (512 dims x 16 rows) += V^T (512 x 16 tokens) . P^T (16 tokens x 16 rows)
-    const int vp = (lr >> 1) & 1;  // chunk parity of this lane's V reads
-    const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ vp) + (lr >> 2)) * 16 + 8 * (lr & 1);
+    if constexpr (!FP8) {
+        const int vp = (lr >> 1) & 1;  // chunk parity of this lane's V reads
+        const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ vp) + (lr >> 2)) * 16 + 8 * (lr & 1);
 #pragma unroll
-    for (int dt = 0; dt < kDV / 16; ++dt) {
-        const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (i16x4 __attribute__((address_space(3))) *)(vt + dt * 2 * 16 * 16));
-        st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[FP8 ? dt / 8 : 0], st.o[dt], 0, 0, 0);
+        for (int dt = 0; dt < kDV / 16; ++dt) {
+            const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 __attribute__((address_space(3))) *)(vt + dt * 2 * 16 * 16));
+            st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[0], st.o[dt], 0, 0, 0);
+        }
+    } else {
+        // dim tiles 2 d2, 2 d2 + 1 (chunks 2 d2, 2 d2 + 1) from one transposed
+        // read: row r = lr / 2 of this lane's 16-lane group is token
+        // 4 lg + r % 4 of chunk 2 d2 + r / 4, bytes 8 (lr & 1) .. + 7; lane lr
+        // receives dim lr of every row, i.e. its group's 4 tokens of dim
+        // 32 d2 + lr (bytes 0..3) and of dim 32 d2 + 16 + lr (bytes 4..7)
+        const int vr = lr >> 1, vtok = 4 * lg + (vr & 3), vch = vr >> 2;
+#pragma unroll
+        for (int d2 = 0; d2 < kDV / 32; ++d2) {
+            const int c = 2 * d2 + vch;
+            const auto cv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (i32x2 __attribute__((address_space(3))) *)(S + slot8(c, vtok) + 8 * (lr & 1)));
+            const bf16x8 v8 = codes8_to_bf16((unsigned)cv[0], (unsigned)cv[1]);
+            const i16x4 va = __builtin_bit_cast(i16x4, (bf16x4){v8[0], v8[1], v8[2], v8[3]});
+            const i16x4 vb = __builtin_bit_cast(i16x4, (bf16x4){v8[4], v8[5], v8[6], v8[7]});
+            const int dt = 2 * d2;
+            st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pf[dt / 8], st.o[dt], 0, 0, 0);
+            st.o[dt + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pf[dt / 8], st.o[dt + 1], 0, 0, 0);
+        }
     }
 }
 
@@ -230,7 +258,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
     const int32_t *__restrict__ meta, const int32_t *__restrict__ split_base) {
     // The read-only tables arrive as separate restrict-qualified arguments so
     // that their uniform reads compile to scalar loads.
-    constexpr int kWaveLds = FP8 ? (2 * kSliceFp8 + kSliceBf16) : (2 * kSliceBf16);
+    // per wave: two bf16 slices, or three FP8 slices (two in flight)
+    constexpr int kWaveLds = FP8 ? 3 * kSliceFp8 : 2 * kSliceBf16;
     static_assert(4 * (kWaves * kRows * kXStride + 3 * kWaves * kRows) <= kWaves * kWaveLds,
                   "the merge buffers fit in the slice buffers");
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWaves * kWaveLds];
@@ -251,8 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
     const int j_first = mrow[1], b_last = mrow[2], j_last = mrow[3], split_first = mrow[4];
 
     lds_u8 *wbase = smem + w * kWaveLds;
-    const unsigned buf_addr[2] = {lds_addr(wbase), lds_addr(wbase + (FP8 ? kSliceFp8 : kSliceBf16))};
-    lds_u8 *bf_slice = wbase + 2 * kSliceFp8;  // FP8 only: dequantised slice
+    const unsigned buf_addr[2] = {lds_addr(wbase), lds_addr(wbase + kSliceBf16)};  // bf16
 
     const int row0 = rg * kRows;
     const int row = row0 + lr;
@@ -271,7 +299,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
         const int32_t *bt = block_table + (int64_t)b * a.bt_stride;
 
         auto tok_last_of = [&](int j) { return (j == npages - 1) ? (L - 1 - j * kPage) : (kPage - 1); };
-        issue_slice<FP8>(kv, bt[j0], tok_last_of(j0), w, lane, buf_addr[0]);
+        auto buf8 = [&](int i) { return lds_addr(wbase) + i * kSliceFp8; };  // FP8
+        if constexpr (!FP8) {
+            issue_slice<FP8>(kv, bt[j0], tok_last_of(j0), w, lane, buf_addr[0]);
+        } else {
+            issue_slice<FP8>(kv, bt[j0], tok_last_of(j0), w, lane, buf8(0));
+            if (j0 < j1) issue_slice<FP8>(kv, bt[j0 + 1], tok_last_of(j0 + 1), w, lane, buf8(1));
+        }
 
         // Q^T operand: lane holds dims 32*ks + 8*lg .. +8 of query row `row`
         bf16x8 qf[kDQk / 32];
@@ -290,23 +324,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
         st.lsum = 0.f;
         st.wsum = 0.f;
 
-        int phys_ahead = (j0 < j1) ? bt[j0 + 1] : 0;
-        for (int j = j0; j <= j1; ++j) {
-            const int cur = (j - j0) & 1;
-            if (j < j1) {
-                issue_slice<FP8>(kv, phys_ahead, tok_last_of(j + 1), w, lane, buf_addr[cur ^ 1]);
-                phys_ahead = (j + 2 <= j1) ? bt[j + 2] : 0;
-                wait_vmcnt<FP8 ? kLoadsFp8 : kLoadsBf16>();
-            } else {
-                wait_vmcnt<0>();
+        if constexpr (!FP8) {
+            int phys_ahead = (j0 < j1) ? bt[j0 + 1] : 0;
+            for (int j = j0; j <= j1; ++j) {
+                const int cur = (j - j0) & 1;
+                if (j < j1) {
+                    issue_slice<FP8>(kv, phys_ahead, tok_last_of(j + 1), w, lane, buf_addr[cur ^ 1]);
+                    phys_ahead = (j + 2 <= j1) ? bt[j + 2] : 0;
+                    wait_vmcnt<kLoadsBf16>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                const lds_u8 *S = wbase + cur * kSliceBf16;
+                f32x4 tsc[4];
+                attend_slice<FP8>(S, qf, st, lane, j * kPage + kSlice * w, n_visible, a.scale_log2, tsc);
             }
-            const lds_u8 *S = wbase + cur * (FP8 ? kSliceFp8 : kSliceBf16);
-            f32x4 tsc[4];
-            if constexpr (FP8) {
-                dequant_slice(S, bf_slice, lane, tsc);
-                S = bf_slice;
+        } else {
+            // three slices: page j + 2 is loaded while page j is processed
+            int phys_ahead = (j0 + 2 <= j1) ? bt[j0 + 2] : 0;
+            for (int j = j0; j <= j1; ++j) {
+                const int cur = (j - j0) % 3;
+                if (j + 2 <= j1) {
+                    issue_slice<FP8>(kv, phys_ahead, tok_last_of(j + 2), w, lane, buf8((cur + 2) % 3));
+                    phys_ahead = (j + 3 <= j1) ? bt[j + 3] : 0;
+                    wait_vmcnt<2 * kLoadsFp8>();
+                } else if (j < j1) {
+                    wait_vmcnt<kLoadsFp8>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                const lds_u8 *S = wbase + cur * kSliceFp8;
+                // the lane's 4 tokens' tile scales (chunk 32 is not swizzled)
+                f32x4 tsc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tsc[i] = *(const f32x4 __attribute__((address_space(3))) *)(S + slot8(32, 4 * lg + i));
+                attend_slice<FP8>(S, qf, st, lane, j * kPage + kSlice * w, n_visible, a.scale_log2, tsc);
             }
-            attend_slice<FP8>(S, qf, st, lane, j * kPage + kSlice * w, n_visible, a.scale_log2, tsc);
         }
 
         // ---- merge the 4 waves' states and write the result
