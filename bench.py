@@ -92,7 +92,8 @@ class Runner:
         self.batch = seqlens.shape[0]
         self.bytes = W.algorithmic_bytes(seqlens, self.s_q, self.h_q, self.fp8)
         self.flops = W.algorithmic_flops(seqlens, self.s_q, self.h_q, self.causal)
-        self.num_parts = mla.default_num_parts(self.s_q, self.h_q, fp8=self.fp8)
+        self.num_parts = mla.default_num_parts(self.s_q, self.h_q, fp8=self.fp8, batch=self.batch,
+                                               max_seqlen=int(seqlens.max()))
         dev = self.q.device
         self.meta = torch.empty((self.num_parts, mla.META_INTS), dtype=torch.int32, device=dev)
         self.split_base = torch.empty((self.batch + 1,), dtype=torch.int32, device=dev)

@@ -107,9 +107,24 @@ int mla_plan_overhead(int s_q, int h_q);
  * bf16, 1 = FP8 records) and for sparse decode (sparse = 1; s_q is then
  * ignored: the plan covers one-token problems), whose kernels may run a part
  * on a different number of work-groups.  Any num_parts gives the same result;
- * these sizes fill the GPU in one round. */
+ * these sizes fill the GPU in one round.
+ *
+ * mla_default_num_parts_for also takes the batch and the longest request
+ * (max_seqlen tokens; the block table's width times 64 will do) and returns
+ * the size this library measures fastest: for 128 query rows per request
+ * (s_q * h_q = 128) over a bf16 cache with at least 48 pages per part at one
+ * part per CU, one part per CU (the CU count rounded up to a multiple of 8);
+ * otherwise mla_default_num_parts_ex's size.
+ *
+ * Which kernel a dense decode runs follows from the plan: 128-row requests
+ * over a bf16 cache run on the 128-row kernel (one work-group per part) when
+ * num_parts >= the device's CU count, and on the 64-row kernel (two
+ * work-groups per part) otherwise.  Both give the same result within the
+ * tolerance. */
 int mla_default_num_parts(int device, int s_q, int h_q);
 int mla_default_num_parts_ex(int device, int s_q, int h_q, int kv_format, int sparse);
+int mla_default_num_parts_for(int device, int batch, int max_seqlen, int s_q, int h_q,
+                              int kv_format, int sparse);
 
 /*
  * Split-KV plan.  Cuts the batch's pages into num_parts contiguous pieces of
@@ -201,13 +216,14 @@ mla_status mla_decode_combine(const int32_t *split_base, int batch, int s_q, int
  * Allocation-free decode, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): mla_decode_fwd / mla_decode_fwd_fp8 (kv_format 0 / 1) with the
- * plan made inside the call (mla_default_num_parts_ex parts) and the plan and
- * the split workspace held in the library's own scratch, a fixed device array
- * of MLA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
- * that GPU until the process ends.  The call allocates and frees nothing;
- * the caller passes inputs and outputs as for mla_decode_fwd.  Problems whose
- * plan and workspace need more than the scratch (mla_noalloc_scratch_need
- * returns the need on the current device, 0 for bad arguments) get
+ * plan made inside the call (mla_default_num_parts_for parts, with max_seqlen
+ * = 64 * block_table_stride) and the plan and the split workspace held in the
+ * library's own scratch, a fixed device array of MLA_NOALLOC_SCRATCH_BYTES per
+ * GPU, held from the library's first use on that GPU until the process ends.
+ * The call allocates and frees nothing; the caller passes inputs and outputs
+ * as for mla_decode_fwd.  Problems whose plan and workspace need more than
+ * the scratch (mla_noalloc_scratch_need returns the need on the current
+ * device for the larger plan the call may make, 0 for bad arguments) get
  * MLA_ERR_WORKSPACE before any launch.  Every call on one GPU shares that
  * GPU's scratch: calls that overlap in time on one GPU (different streams,
  * or threads) race and must be serialised by the caller.  Nothing in the

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "mla_plan_overhead": (_I, [_I, _I]),
     "mla_default_num_parts": (_I, [_I, _I, _I]),
     "mla_default_num_parts_ex": (_I, [_I, _I, _I, _I, _I]),
+    "mla_default_num_parts_for": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "mla_get_metadata": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "mla_get_metadata_host": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "mla_decode_fwd": (_I, [_P, _P, _I64, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P, _I, _P, _SZ,
@@ -108,27 +109,35 @@ def workspace_bytes(batch, s_q, h_q, num_parts):
     return lib().mla_workspace_bytes(batch, s_q, h_q, num_parts)
 
 
-def default_num_parts(s_q, h_q, device=None, fp8=False, sparse=False):
+def default_num_parts(s_q, h_q, device=None, fp8=False, sparse=False, batch=None, max_seqlen=None):
     """Plan size that fills the GPU in one round for this shape and cache
-    format (sparse=True: sparse decode of h_q heads)."""
+    format (sparse=True: sparse decode of h_q heads).  With batch and
+    max_seqlen (the longest request, or an upper bound), the size the library
+    measures fastest for them (mla_default_num_parts_for)."""
     dev = torch.cuda.current_device() if device is None else int(device)
-    n = lib().mla_default_num_parts_ex(dev, s_q, h_q, 1 if fp8 else 0, 1 if sparse else 0)
+    if batch is not None and max_seqlen is not None:
+        n = lib().mla_default_num_parts_for(dev, int(batch), int(max_seqlen), s_q, h_q, 1 if fp8 else 0,
+                                            1 if sparse else 0)
+    else:
+        n = lib().mla_default_num_parts_ex(dev, s_q, h_q, 1 if fp8 else 0, 1 if sparse else 0)
     if n < 0:
         _check(n, "mla_default_num_parts")
     return n
 
 
-def get_metadata(seqlens, s_q, h_q, num_parts=None, fp8=False):
+def get_metadata(seqlens, s_q, h_q, num_parts=None, fp8=False, max_seqlen=None):
     """Plan split-KV work on the GPU.  seqlens: int32 CUDA tensor [batch];
-    without num_parts, the size that suits the cache format (fp8).
+    without num_parts, the size that suits the cache format (fp8) and, given
+    max_seqlen (the longest request or an upper bound), the batch's lengths.
 
     Returns (meta int32 [num_parts, 8], split_base int32 [batch + 1], num_parts).
     """
     if seqlens.dtype != torch.int32 or not seqlens.is_cuda or not seqlens.is_contiguous():
         raise MlaError("seqlens must be a contiguous int32 CUDA tensor")
-    if num_parts is None:
-        num_parts = default_num_parts(s_q, h_q, seqlens.device.index, fp8=fp8)
     batch = seqlens.shape[0]
+    if num_parts is None:
+        num_parts = default_num_parts(s_q, h_q, seqlens.device.index, fp8=fp8, batch=batch,
+                                      max_seqlen=max_seqlen)
     meta = torch.empty((num_parts, META_INTS), dtype=torch.int32, device=seqlens.device)
     split_base = torch.empty((batch + 1,), dtype=torch.int32, device=seqlens.device)
     _check(lib().mla_get_metadata(_ptr(seqlens), batch, s_q, h_q, num_parts, _ptr(meta),
@@ -311,7 +320,9 @@ def decode(q, kcache, block_table, seqlens, softmax_scale, causal, meta=None, sp
                       "block table / seqlens")
     b, s_q, h_q, _ = q.shape
     if meta is None and split_base is None:
-        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts, fp8=fp8)
+        # the table's width bounds the longest request
+        meta, split_base, num_parts = get_metadata(seqlens, s_q, h_q, num_parts, fp8=fp8,
+                                                   max_seqlen=block_table.shape[1] * PAGE)
     _check_plan(q, meta, split_base, num_parts)
     out, lse = _outputs(q, out, lse)
     workspace = _workspace(q, num_parts, workspace)

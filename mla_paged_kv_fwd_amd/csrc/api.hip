@@ -45,24 +45,47 @@ static_assert(MLA_D_QK == mla::kDQk && MLA_D_V == mla::kDV && MLA_PAGE == mla::k
 
 namespace {
 
-// Kernel choice: 128 query rows per work-group for 128-row requests over a
-// bf16 cache (dense decode); 64 query rows per work-group with specialised
-// score / value waves when a request has at least 32 rows (32 rows leave half
-// the group as padding: the problem is memory-bound and reads each page once
-// instead of twice); 16 rows per work-group otherwise.  With 256 or 512 rows
-// the 64-row kernel is as fast or faster (a part's row groups share its
-// half-pages through L2, and with half the parts per CU fewer requests are
-// split, so fewer partial results are written and merged).
-bool use_rows128(int M, int kv_format, int token_list) {
-    return M == 128 && kv_format == 0 && !token_list;
+// Kernel choice.  64 query rows per work-group with specialised score /
+// value waves when a request has at least 32 rows (32 rows leave half the
+// group as padding: the problem is memory-bound and reads each page once
+// instead of twice); 16 rows per work-group otherwise.  128-row requests over
+// a bf16 cache (dense decode) run on the 128-row kernel instead when the plan
+// has at least one part per CU: it runs a part on one work-group (the 64-row
+// kernel on two), so such plans fill the chip with it, and it is the faster
+// kernel when the parts are long (it halves the LDS traffic per row; with
+// short parts its larger fixed cost per segment loses).
+// mla_default_num_parts_for plans one part per CU exactly when the parts are
+// long.  With 256 or 512 rows the 64-row kernel is as fast or faster (a
+// part's row groups share its half-pages through L2, and with half the parts
+// per CU fewer requests are split, so fewer partial results are written and
+// merged).
+bool use_rows128(int M, int kv_format, int token_list, int num_parts, int cus) {
+    return M == 128 && kv_format == 0 && !token_list && num_parts >= cus;
 }
 bool use_rows64(int M) { return M >= 32; }
 int rows64_groups(int M) { return (M + 63) / 64; }  // M = 32 pads one group
-// work-groups per part of the kernel a call runs on
-int groups_per_part(int M, int kv_format, int token_list) {
-    if (use_rows128(M, kv_format, token_list)) return M / 128;
+// work-groups per part of the 64- and 16-row kernels
+int groups_per_part(int M, int token_list) {
     if (use_rows64(M) || token_list) return rows64_groups(M);
     return M / 16;
+}
+// Pages per part from which a 128-row plan with one part per CU beats the
+// 64-row kernel's plan (measured: 32 pages per part lose or tie, 64 win).
+constexpr int kRows128MinPagesPerPart = 48;
+
+// CUs of each device, queried once (0: not yet)
+int g_cu_count[64];
+// CU count of `device`, or a status code (< 0)
+int cu_count(int device) {
+    if (device < 0 || device >= 64) return MLA_ERR_INVALID_ARG;
+    if (g_cu_count[device] <= 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+            cus <= 0)
+            return MLA_ERR_HIP;
+        g_cu_count[device] = cus;
+    }
+    return g_cu_count[device];
 }
 
 bool shape_supported(int s_q, int h_q) {
@@ -124,8 +147,12 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     a.causal = causal;
     a.token_list = token_list;
     hipError_t e;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    const int cus = cu_count(dev);
+    if (cus < 0) return (mla_status)cus;
     // token lists always run on the 64-row kernels (M = 16 pads one group)
-    if (use_rows128(M, kv_format, token_list)) {
+    if (use_rows128(M, kv_format, token_list, num_parts, cus)) {
         a.row_groups = M / 128;
         e = mla::launch_decode_rows128(a, (hipStream_t)stream);
     } else if (use_rows64(M) || token_list) {
@@ -239,7 +266,6 @@ mla_status decode_sparse_impl(const void *q, const void *kcache, int kv_format, 
                         out, lse, stream);
 }
 
-int g_cu_count[64];
 
 // Scratch of the allocation-free decode (mla_decode_fwd_noalloc): the plan and
 // the split workspace of one call, in a file-scope device array that every
@@ -296,22 +322,32 @@ int mla_plan_overhead(int s_q, int h_q) { return mla::plan_overhead(s_q, h_q); }
 int mla_default_num_parts_ex(int device, int s_q, int h_q, int kv_format, int sparse) {
     if (!shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
     if ((kv_format != 0 && kv_format != 1) || (sparse != 0 && sparse != 1)) return MLA_ERR_INVALID_ARG;
-    if (device < 0 || device >= 64) return MLA_ERR_INVALID_ARG;
-    if (g_cu_count[device] <= 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-            cus <= 0)
-            return MLA_ERR_HIP;
-        g_cu_count[device] = cus;
-    }
+    const int cus = cu_count(device);
+    if (cus < 0) return cus;
     // one work-group per CU, all in one round: a part spans as many
     // work-groups as the kernel that runs it has row groups (sparse decode
     // plans one-token problems of h_q rows)
     const int M = sparse ? h_q : s_q * h_q;
-    int parts = g_cu_count[device];
-    parts = parts / groups_per_part(M, kv_format, sparse);
+    int parts = cus / groups_per_part(M, sparse);
     parts = parts < 8 ? 8 : parts;
     return (parts + 7) / 8 * 8;
+}
+
+int mla_default_num_parts_for(int device, int batch, int max_seqlen, int s_q, int h_q, int kv_format,
+                              int sparse) {
+    const int parts = mla_default_num_parts_ex(device, s_q, h_q, kv_format, sparse);
+    if (parts < 0) return parts;
+    if (batch < 0 || max_seqlen < 0) return MLA_ERR_INVALID_ARG;
+    const int cus = cu_count(device);
+    if (cus < 0) return cus;
+    // 128-row requests over a bf16 cache with long parts: one part per CU,
+    // which runs them on the 128-row kernel
+    const int64_t pages = (int64_t)batch * (((int64_t)max_seqlen + mla::kPage - 1) / mla::kPage);
+    const int one_per_cu = (cus + 7) / 8 * 8;
+    if (!sparse && kv_format == 0 && s_q * h_q == 128 &&
+        pages >= (int64_t)kRows128MinPagesPerPart * one_per_cu)
+        return one_per_cu;
+    return parts;
 }
 
 int mla_default_num_parts(int device, int s_q, int h_q) {
@@ -398,8 +434,16 @@ size_t mla_noalloc_scratch_need(int batch, int s_q, int h_q, int kv_format) {
     if (!shape_supported(s_q, h_q) || batch > mla::kMaxBatch) return 0;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const int parts = mla_default_num_parts_ex(dev, s_q, h_q, kv_format, 0);
+    // the larger of the plans the call may make (one part per CU for
+    // 128-row requests with long contexts)
+    int parts = mla_default_num_parts_ex(dev, s_q, h_q, kv_format, 0);
     if (parts <= 0) return 0;
+    if (s_q * h_q == 128 && kv_format == 0) {
+        const int cus = cu_count(dev);
+        if (cus <= 0) return 0;
+        const int one_per_cu = (cus + 7) / 8 * 8;
+        parts = parts > one_per_cu ? parts : one_per_cu;
+    }
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return up((size_t)parts * mla::kMetaInts * 4) + up(((size_t)batch + 1) * 4) +
            workspace_bytes(batch, s_q, h_q, parts);
@@ -420,7 +464,10 @@ mla_status mla_decode_fwd_noalloc(const void *q, const void *kcache, int kv_form
     if (batch > mla::kMaxBatch || !shape_supported(s_q, h_q)) return MLA_ERR_UNSUPPORTED;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
-    const int parts = mla_default_num_parts_ex(dev, s_q, h_q, kv_format, 0);
+    // plan size from the longest request the table can hold
+    const int64_t max_len = (int64_t)block_table_stride * mla::kPage;
+    const int parts = mla_default_num_parts_for(dev, batch, max_len < INT32_MAX ? (int)max_len : INT32_MAX,
+                                                s_q, h_q, kv_format, 0);
     if (parts <= 0) return parts < 0 ? (mla_status)parts : MLA_ERR_HIP;
     // scratch layout: meta, split_base, then the split workspace (256-byte aligned)
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };

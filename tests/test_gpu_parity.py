@@ -201,9 +201,9 @@ def test_full_size_workloads_on_sampled_rows(name):
 
 
 ROWS128 = [
-    # seqlens, s_q, h_q, causal, num_parts: lengths on both sides of the
-    # 16-token unit and 32-token step boundaries of the 128-row kernel, parts
-    # that walk many requests, and four row groups (M = 512)
+    # seqlens, s_q, h_q, causal, num_parts: 128 or more rows per request on
+    # plans of a few parts (the 64-row kernel, parts that walk many requests)
+    # and four row groups (M = 512)
     ([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 95, 96, 97, 1000, 2500], 1, 128, False, 3),
     ([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 95, 96, 97, 1000, 2500], 1, 128, False, 37),
     ([2, 17, 33, 250, 1200], 2, 64, True, 5),
@@ -220,3 +220,49 @@ def test_128_row_groups_match_oracle(seqlens, s_q, h_q, causal, num_parts):
     ref_out, ref_lse = oracle_all(case)
     compare(out, lse, ref_out, ref_lse,
             f"128-row {seqlens} s_q={s_q} h_q={h_q} causal={causal} parts={num_parts}")
+
+
+def _one_part_per_cu():
+    import mla_paged_kv_fwd_amd as mla
+
+    # a long context for 128 rows per request: the plan of one part per CU
+    return mla.default_num_parts(1, 128, batch=1, max_seqlen=1 << 24)
+
+
+ROWS128_KERNEL = [
+    # seqlens (repeated), s_q, h_q, causal: 128 rows per request over a bf16
+    # cache on a plan of one part per CU, which runs the 128-row kernel.
+    # Lengths on both sides of its 16-token unit and 32-token step
+    # boundaries, repeated so that parts walk several requests.
+    ([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 95, 96, 97, 1000, 2500], 12, 1, 128, False),
+    ([2, 17, 33, 250, 1200], 40, 2, 64, True),
+    ([4, 18, 34, 251, 900], 30, 4, 32, False),
+]
+
+
+@pytest.mark.parametrize("seqlens,reps,s_q,h_q,causal", ROWS128_KERNEL)
+def test_128_row_kernel_matches_oracle(seqlens, reps, s_q, h_q, causal):
+    parts = _one_part_per_cu()
+    case = W.make_case(seqlens * reps, s_q, h_q, seed=350 + h_q + s_q, causal=causal, spare_pages=2,
+                       poison=True)
+    print(f"128-row kernel: {len(case.seqlens)} requests s_q={s_q} h_q={h_q} parts={parts}", flush=True)
+    out, lse = run_gpu(case, num_parts=parts)
+    ref_out, ref_lse = oracle_all(case)
+    compare(out, lse, ref_out, ref_lse, f"128-row kernel {len(case.seqlens)} requests s_q={s_q} h_q={h_q}")
+
+
+def test_plan_size_follows_the_context_length():
+    import mla_paged_kv_fwd_amd as mla
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    one_per_cu = (cus + 7) // 8 * 8
+    assert _one_part_per_cu() == one_per_cu
+    short = mla.default_num_parts(1, 128)  # the 64-row kernel's plan: two work-groups per part
+    assert short == max(8, (cus // 2 + 7) // 8 * 8)
+    pages_needed = 48 * one_per_cu
+    assert mla.default_num_parts(1, 128, batch=pages_needed, max_seqlen=64) == one_per_cu
+    assert mla.default_num_parts(1, 128, batch=pages_needed - 1, max_seqlen=64) == short
+    # other shapes and the FP8 cache keep the one-round size of their kernel
+    assert mla.default_num_parts(2, 128, batch=64, max_seqlen=1 << 20) == mla.default_num_parts(2, 128)
+    assert mla.default_num_parts(1, 128, fp8=True, batch=64, max_seqlen=1 << 20) == \
+        mla.default_num_parts(1, 128, fp8=True)
