@@ -611,7 +611,7 @@ def roofline(rep, workload, ceil=None):
     cfg = W.CONFIGS[workload]
     rows = cfg["s_q"] * cfg["h_q"]
     if rows < 32:
-        kernel = "decode_rowgroup_kernel<%s>" % ("true" if cfg["fp8"] else "false")
+        kernel = "decode_rowgroup_kernel<%s, false>" % ("true" if cfg["fp8"] else "false")
     elif rows == 128 and not cfg["fp8"]:
         kernel = "decode_rows128_kernel"
     else:

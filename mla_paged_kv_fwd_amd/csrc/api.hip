@@ -66,7 +66,8 @@ bool use_rows64(int M) { return M >= 32; }
 int rows64_groups(int M) { return (M + 63) / 64; }  // M = 32 pads one group
 // work-groups per part of the 64- and 16-row kernels
 int groups_per_part(int M, int token_list) {
-    if (use_rows64(M) || token_list) return rows64_groups(M);
+    (void)token_list;  // token lists run on the same kernels as dense decode
+    if (use_rows64(M)) return rows64_groups(M);
     return M / 16;
 }
 // Pages per part from which a 128-row plan with one part per CU beats the
@@ -151,11 +152,11 @@ mla_status decode_attn_impl(const void *q, const void *kcache, int kv_format, in
     if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
     const int cus = cu_count(dev);
     if (cus < 0) return (mla_status)cus;
-    // token lists always run on the 64-row kernels (M = 16 pads one group)
+    // token lists run on the 64-row kernels, or on the 16-row kernel for M = 16
     if (use_rows128(M, kv_format, token_list, num_parts, cus)) {
         a.row_groups = M / 128;
         e = mla::launch_decode_rows128(a, (hipStream_t)stream);
-    } else if (use_rows64(M) || token_list) {
+    } else if (use_rows64(M)) {
         a.row_groups = rows64_groups(M);
         e = kv_format == 1 ? mla::launch_decode_rows64_fp8(a, (hipStream_t)stream)
                            : mla::launch_decode_rows64(a, (hipStream_t)stream);

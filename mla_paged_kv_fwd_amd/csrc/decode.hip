@@ -36,6 +36,15 @@
 // The swizzle puts the two chunks of a V read on different banks (tokens 8
 // apart are 32 banks apart); the K reads of 32 lanes are 256 contiguous
 // bytes either way.
+//
+// Token-list mode (sparse decode, kList): a "request" is one query token's
+// list of cache token ids (physical page * 64 + slot) and the block-table
+// argument holds the lists; "page" j of a list is its positions 64 j .. +63.
+// Each lane loads the id of the token whose chunks it moves and takes the
+// token's record from there, so the listed rows or records are read once, in
+// place.  The ids of page j + (slices per wave - 1) are loaded one page ahead,
+// before that page's loads, so waiting for an id never waits on a younger
+// load.
 #include <math.h>
 
 #include "common.h"
@@ -87,6 +96,31 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
             int cidx = 4 * s + lg;
             cidx = cidx < 40 ? cidx : 40;  // slots past chunk 40 are padding
             dma16(mine + cidx * 16, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
+        }
+    }
+}
+
+// Token-list mode: the token whose chunks this lane moves (before clamping
+// to the page's last valid one), and the direct-to-LDS loads of a slice from
+// that token's row or record `rec`.
+template <bool FP8>
+__device__ __forceinline__ int lane_token(int w, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    return kSlice * w + (lr ^ ((FP8 ? 8 : 4) * (lg & 1)));
+}
+template <bool FP8>
+__device__ __forceinline__ void issue_rec(const unsigned char *rec, int lane, unsigned lds_dst) {
+    const int lg = lane >> 4;
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int s = 0; s < kLoadsBf16; ++s)
+            dma16(rec + lg * 16 + s * 64, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
+    } else {
+#pragma unroll
+        for (int s = 0; s < kLoadsFp8; ++s) {
+            int cidx = 4 * s + lg;
+            cidx = cidx < 40 ? cidx : 40;  // slots past chunk 40 are padding
+            dma16(rec + cidx * 16, __builtin_amdgcn_readfirstlane(lds_dst + s * 1024));
         }
     }
 }
@@ -251,7 +285,7 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
     }
 }
 
-template <bool FP8>
+template <bool FP8, bool kList>
 __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
     const DecodeArgs a, const uint16_t *__restrict__ q, const unsigned char *__restrict__ kv,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ seqlens,
@@ -300,7 +334,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
 
         auto tok_last_of = [&](int j) { return (j == npages - 1) ? (L - 1 - j * kPage) : (kPage - 1); };
         auto buf8 = [&](int i) { return lds_addr(wbase) + i * kSliceFp8; };  // FP8
-        if constexpr (!FP8) {
+        // token lists: the id of this lane's token in page j, and its row or record
+        constexpr int kRecBytes = FP8 ? kTokBytesFp8 : kTokBytesBf16;
+        const int ltok = lane_token<FP8>(w, lane);
+        auto lane_id = [&](int j) {
+            const int tl = tok_last_of(j);
+            return bt[j * kPage + (ltok < tl ? ltok : tl)];
+        };
+        auto rec_of = [&](int id) { return kv + (int64_t)id * kRecBytes; };
+        int id_ahead = 0;  // token lists: the id of the next page to load
+        if constexpr (kList) {
+            const int id0 = lane_id(j0);
+            const int id1 = (j0 < j1) ? lane_id(j0 + 1) : 0;
+            if constexpr (FP8) id_ahead = (j0 + 2 <= j1) ? lane_id(j0 + 2) : 0;
+            issue_rec<FP8>(rec_of(id0), lane, FP8 ? buf8(0) : buf_addr[0]);
+            if constexpr (FP8) {
+                if (j0 < j1) issue_rec<FP8>(rec_of(id1), lane, buf8(1));
+            } else {
+                id_ahead = id1;
+            }
+        } else if constexpr (!FP8) {
             issue_slice<FP8>(kv, bt[j0], tok_last_of(j0), w, lane, buf_addr[0]);
         } else {
             issue_slice<FP8>(kv, bt[j0], tok_last_of(j0), w, lane, buf8(0));
@@ -324,7 +377,45 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
         st.lsum = 0.f;
         st.wsum = 0.f;
 
-        if constexpr (!FP8) {
+        if constexpr (kList && !FP8) {
+            for (int j = j0; j <= j1; ++j) {
+                const int cur = (j - j0) & 1;
+                if (j < j1) {
+                    // the next page's id first, then this page's successor's loads
+                    const bool more = j + 2 <= j1;
+                    const int id_next = more ? lane_id(j + 2) : 0;
+                    issue_rec<FP8>(rec_of(id_ahead), lane, buf_addr[cur ^ 1]);
+                    id_ahead = id_next;
+                    if (more) wait_vmcnt<kLoadsBf16 + 1>(); else wait_vmcnt<kLoadsBf16>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                const lds_u8 *S = wbase + cur * kSliceBf16;
+                f32x4 tsc[4];
+                attend_slice<FP8>(S, qf, st, lane, j * kPage + kSlice * w, n_visible, a.scale_log2, tsc);
+            }
+        } else if constexpr (kList) {
+            for (int j = j0; j <= j1; ++j) {
+                const int cur = (j - j0) % 3;
+                if (j + 2 <= j1) {
+                    const bool more = j + 3 <= j1;
+                    const int id_next = more ? lane_id(j + 3) : 0;
+                    issue_rec<FP8>(rec_of(id_ahead), lane, buf8((cur + 2) % 3));
+                    id_ahead = id_next;
+                    if (more) wait_vmcnt<2 * kLoadsFp8 + 1>(); else wait_vmcnt<2 * kLoadsFp8>();
+                } else if (j < j1) {
+                    wait_vmcnt<kLoadsFp8>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                const lds_u8 *S = wbase + cur * kSliceFp8;
+                f32x4 tsc[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tsc[i] = *(const f32x4 __attribute__((address_space(3))) *)(S + slot8(32, 4 * lg + i));
+                attend_slice<FP8>(S, qf, st, lane, j * kPage + kSlice * w, n_visible, a.scale_log2, tsc);
+            }
+        } else if constexpr (!FP8) {
             int phys_ahead = (j0 < j1) ? bt[j0 + 1] : 0;
             for (int j = j0; j <= j1; ++j) {
                 const int cur = (j - j0) & 1;
@@ -440,11 +531,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream) {
     const int groups8 = (a.num_parts + 7) / 8;
     const dim3 grid(groups8 * 8 * a.row_groups), block(kThreads);
-    if (fp8)
-        hipLaunchKernelGGL(decode_rowgroup_kernel<true>, grid, block, 0, stream, a, a.q, a.kv,
+    if (fp8 && a.token_list)
+        hipLaunchKernelGGL((decode_rowgroup_kernel<true, true>), grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
+    else if (fp8)
+        hipLaunchKernelGGL((decode_rowgroup_kernel<true, false>), grid, block, 0, stream, a, a.q, a.kv,
+                           a.block_table, a.seqlens, a.meta, a.split_base);
+    else if (a.token_list)
+        hipLaunchKernelGGL((decode_rowgroup_kernel<false, true>), grid, block, 0, stream, a, a.q, a.kv,
                            a.block_table, a.seqlens, a.meta, a.split_base);
     else
-        hipLaunchKernelGGL(decode_rowgroup_kernel<false>, grid, block, 0, stream, a, a.q, a.kv,
+        hipLaunchKernelGGL((decode_rowgroup_kernel<false, false>), grid, block, 0, stream, a, a.q, a.kv,
                            a.block_table, a.seqlens, a.meta, a.split_base);
     return hipGetLastError();
 }

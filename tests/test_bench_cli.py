@@ -22,9 +22,9 @@ def test_measured_traffic_matches_sources_or_is_none():
 
     # every traffic line names a kernel and workload; a value comes back only
     # while the listed sources still hash to what was profiled
-    for kernel, workload in [("decode_rowgroup_kernel<false>", "membound"),
+    for kernel, workload in [("decode_rowgroup_kernel<false, false>", "membound"),
                              ("decode_rows64_kernel<false>", "computebound"),
-                             ("decode_rows64_kernel<false>", "longctx"),
+                             ("decode_rows128_kernel", "longctx"),
                              ("decode_rows64_fp8_kernel<false>", "fp8")]:
         t = bench.measured_traffic(kernel, workload)
         assert t is None or t > 0
@@ -37,7 +37,7 @@ def test_headline_profile_matches_the_kernel_source():
     sys.path.insert(0, ROOT)
     import bench
 
-    t = bench.measured_traffic("decode_rowgroup_kernel<false>", "membound")
+    t = bench.measured_traffic("decode_rowgroup_kernel<false, false>", "membound")
     assert t is not None, "profiles/decode_rowgroup_kernel_membound.md is stale: re-profile"
     assert 600e6 < t < 700e6  # 608.5 MB algorithmic per launch
 
