@@ -46,6 +46,31 @@ def test_noalloc_decode_equals_decode(fp8):
                 f"noalloc fp8={fp8} {seqlens}")
 
 
+def test_noalloc_long_context_plan_equals_decode():
+    # 128 rows per request with parts long enough for one part per CU: both
+    # calls plan one part per CU (the 128-row kernel) from the table's width
+    import mla_paged_kv_fwd_amd as mla
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    one_per_cu = (cus + 7) // 8 * 8
+    length = 8192
+    batch = -(-48 * one_per_cu // (length // 64))
+    assert mla.default_num_parts(1, 128, batch=batch, max_seqlen=length) == one_per_cu
+    print(f"noalloc long context: batch {batch} x {length}, parts {one_per_cu}", flush=True)
+    sl = np.full(batch, length, dtype=np.int32)
+    q, kc, bt, slt = W.make_device_inputs(sl, 1, 128, False, seed=502)
+    scale = 1.0 / np.sqrt(W.D_QK)
+    assert 0 < mla.noalloc_scratch_need(batch, 1, 128) <= (128 << 20)
+    ref_out, ref_lse = mla.decode(q, kc, bt, slt, scale, False)
+    out = torch.full_like(ref_out, float("nan"))
+    lse = torch.full_like(ref_lse, float("nan"))
+    mla.decode_noalloc(q, kc, bt, slt, scale, False, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
 def test_noalloc_refuses_problems_beyond_its_scratch():
     import mla_paged_kv_fwd_amd as mla
 
