@@ -30,7 +30,11 @@
 // (164 dwords, 36 mod 64 banks) both the 16-byte K reads of 16 tokens and the
 // transposed V reads of 8 tokens hit distinct banks, so no swizzle is needed.
 // (Tokens 16 apart share banks, so 8-byte K reads, served 32 lanes at a time,
-// would conflict two ways.)
+// would conflict two ways.)  Token order: MFMA row m of a 16-token k-step
+// holds token tok16(m) = 8 m3 + 4 m1 + 2 m0 + m2 (m = 8 m3 + 4 m2 + 2 m1 + m0),
+// in the K reads, the score scales and mask, and the V reads and scales
+// alike, so the 32-lane passes of the transposed V reads cover the even and
+// then the odd tokens of a k-step, whose 32-byte pieces sit on disjoint banks.
 //
 // Token-list mode (sparse decode, kList): each "request" is one query token's
 // list of cache token ids; the score waves stage the ids of half-page t + 3 in
@@ -103,6 +107,12 @@ __device__ __forceinline__ void score_done(f32x16 (&s)[5]) {
 // load block 10 (the same bytes to the same place), which keeps their code
 // identical.
 __device__ __forceinline__ int first_block(int v) { return v ? kDmaFp8 - kDmaWave : 0; }
+
+// Token of MFMA row m (0..31) of a half-page: within each 16-token k-step,
+// bits (m3 m2 m1 m0) -> 8 m3 + 4 m1 + 2 m0 + m2.
+__device__ __forceinline__ int tok_of_row(int m) {
+    return (m & 16) + 8 * ((m >> 3) & 1) + 4 * ((m >> 1) & 1) + 2 * (m & 1) + ((m >> 2) & 1);
+}
 
 // Value wave v's direct-to-LDS loads of a half-page: its k-th load is 1 KB
 // block i = first_block(v) + k, bytes [1024 i, 1024 i + 1024) of the 32
@@ -227,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
         const int qi = row_q / a.h_q;
         const float c = a.scale_log2;  // > 0
         const float grow = kGrowLog2 / c;
-        const int krec = kTokBytesFp8 * l32;  // this lane's K token record in a slot
+        const int krec = kTokBytesFp8 * tok_of_row(l32);  // this lane's K token record in a slot
         for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
             if constexpr (kList) {
                 stage_first_ids(ids_lds, sg, l32, h);
@@ -284,13 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     int id_next = 0;
                     if (stage) id_next = list_ids(sg, t + 3)[l32];
                     const lds_u8 *S = smem + (t % kRing) * kSlot;
-                    // lane holds tokens 8 (i/4) + 4 h + (i%4) of the half-page for
+                    // lane holds tokens 8 (i/4) + 2 (i%4) + h of the half-page for
                     // its row; a token's four tile scales are the 16 bytes at byte
                     // 512 of its record: all sixteen read now, used after the MFMAs
                     f32x4 sc[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        sc[i] = *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * (i >> 2) + 4 * h + (i & 3)) + kFp8ScalesAt);
+                        sc[i] = *(const lds_f32x4 *)(S + kTokBytesFp8 * (8 * (i >> 2) + 2 * (i & 3) + h) + kFp8ScalesAt);
                     // S^T (32 tokens x 32 rows) per 128-dim tile and for the RoPE dims
                     f32x16 acc[5];
                     // K codes of k-steps 2 pp, 2 pp + 1: the 16 codes at dims
@@ -342,10 +352,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     }
                     const int tok0 = sg.j0 * kPage + t * kHalf;
                     if (tok0 + kHalf > n_visible_all) {  // the causal edge or the segment's end
-                        const int tok_base = tok0 + 4 * h;
+                        const int tok_base = tok0 + h;
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            x[i] = (tok_base + 8 * (i >> 2) + (i & 3) < n_visible) ? x[i] : -INFINITY;
+                            x[i] = (tok_base + 8 * (i >> 2) + 2 * (i & 3) < n_visible) ? x[i] : -INFINITY;
                     }
                     float mloc = x[0];
 #pragma unroll
@@ -408,16 +418,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
             const int v = w - 2, d0 = v * 256;
             // Transposed V reads (ds_read_b64_tr_b8), 32x32x16 A operand of
             // k-step kk, dim tile dt.  The k order must match P^T, which keeps the
-            // score accumulator's order: lane half h = lane / 32 holds tokens
-            // 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step.  16-lane group
-            // g = lane / 16 covers dims d0 + 32 dt + 16 (g & 1) + (lane % 16); its
-            // lanes 2 r, 2 r + 1 point at the r-th of those 8 tokens, 8 codes at
-            // dim offset 8 (lane % 2).
+            // score accumulator's order: lane half h = lane / 32 holds rows
+            // 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step, which are
+            // tokens h + 0, 2, 4, 6 and 8 + h + 0, 2, 4, 6 (tok_of_row).  16-lane
+            // group g = lane / 16 covers dims d0 + 32 dt + 16 (g & 1) + (lane % 16);
+            // its lanes 2 r, 2 r + 1 point at the r-th of those 8 tokens, 8 codes
+            // at dim offset 8 (lane % 2).
             const int g = lane >> 4, i16 = lane & 15, vr = i16 >> 1;
-            const int vtok = 4 * (g >> 1) + (vr & 3) + 8 * (vr >> 2);
+            const int vtok = tok_of_row(4 * (g >> 1) + (vr & 3) + 8 * (vr >> 2));
             const int vrec = kTokBytesFp8 * vtok + d0 + 16 * (g & 1) + 8 * (i16 & 1);
-            // scales of tiles 2 v, 2 v + 1 of this lane's first token (4 (lane / 32))
-            const int vsc = kTokBytesFp8 * (4 * (lane >> 5)) + kFp8ScalesAt + 8 * v;
+            // scales of tiles 2 v, 2 v + 1 of this lane's first token (lane / 32)
+            const int vsc = kTokBytesFp8 * (lane >> 5) + kFp8ScalesAt + 8 * v;
             for_each_segment(mrow, seqlens, split_base, block_table, a.bt_stride, [&](const Segment &sg) {
                 if constexpr (kList) __syncthreads();  // ids of half-pages 0 .. 2 staged
                 list_issue_step(sg, kv, 0, v, lane, ring0, ids_lds);
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                         auto read_scales = [&](int kk, f32x2 (&sc)[8]) {
     #pragma unroll
                             for (int j = 0; j < 8; ++j)
-                                sc[j] = *(const lds_f32x2 *)(Vs + kTokBytesFp8 * (16 * kk + (j & 3) + 8 * (j >> 2)));
+                                sc[j] = *(const lds_f32x2 *)(Vs + kTokBytesFp8 * (16 * kk + 2 * (j & 3) + 8 * (j >> 2)));
                         };
                         // V^T fragment: one dim of the 8 tokens, each code times its
                         // token's scale of tile 2 v + (dt / 4), rounded to bf16
@@ -514,16 +525,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
             const int v = w - 2, d0 = v * 256;
             // Transposed V reads (ds_read_b64_tr_b8), 32x32x16 A operand of
             // k-step kk, dim tile dt.  The k order must match P^T, which keeps the
-            // score accumulator's order: lane half h = lane / 32 holds tokens
-            // 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step.  16-lane group
-            // g = lane / 16 covers dims d0 + 32 dt + 16 (g & 1) + (lane % 16); its
-            // lanes 2 r, 2 r + 1 point at the r-th of those 8 tokens, 8 codes at
-            // dim offset 8 (lane % 2).
+            // score accumulator's order: lane half h = lane / 32 holds rows
+            // 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step, which are
+            // tokens h + 0, 2, 4, 6 and 8 + h + 0, 2, 4, 6 (tok_of_row).  16-lane
+            // group g = lane / 16 covers dims d0 + 32 dt + 16 (g & 1) + (lane % 16);
+            // its lanes 2 r, 2 r + 1 point at the r-th of those 8 tokens, 8 codes
+            // at dim offset 8 (lane % 2).
             const int g = lane >> 4, i16 = lane & 15, vr = i16 >> 1;
-            const int vtok = 4 * (g >> 1) + (vr & 3) + 8 * (vr >> 2);
+            const int vtok = tok_of_row(4 * (g >> 1) + (vr & 3) + 8 * (vr >> 2));
             const int vrec = kTokBytesFp8 * vtok + d0 + 16 * (g & 1) + 8 * (i16 & 1);
-            // scales of tiles 2 v, 2 v + 1 of this lane's first token (4 (lane / 32))
-            const int vsc = kTokBytesFp8 * (4 * (lane >> 5)) + kFp8ScalesAt + 8 * v;
+            // scales of tiles 2 v, 2 v + 1 of this lane's first token (lane / 32)
+            const int vsc = kTokBytesFp8 * (lane >> 5) + kFp8ScalesAt + 8 * v;
             unsigned fo[kDmaWave];  // offsets of the loads of a full half-page
     #pragma unroll
             for (int k = 0; k < kDmaWave; ++k) fo[k] = half_offset(v, k, lane, kHalf - 1);
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rows64_fp8_kernel(
                     const lds_u8 *Vs = smem + (u % kRing) * kSlot + vsc;
     #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        sc[j] = *(const lds_f32x2 *)(Vs + kTokBytesFp8 * (16 * kk + (j & 3) + 8 * (j >> 2)));
+                        sc[j] = *(const lds_f32x2 *)(Vs + kTokBytesFp8 * (16 * kk + 2 * (j & 3) + 8 * (j >> 2)));
                 };
                 // V^T fragment of half-page u: one dim of the 8 tokens (codes), then
                 // each code times its token's scale of tile 2 v + (dt / 4), rounded
