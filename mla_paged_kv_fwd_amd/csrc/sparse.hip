@@ -22,14 +22,19 @@ constexpr int kPrepThreads = 256;
 
 constexpr int kPerThread = 8;  // list entries each thread loads before using any
 
+constexpr int kChunk = kPrepThreads * kPerThread;
+
 // Length of list r: the position of its first negative entry, else topk.
 // All kPrepThreads threads; the result in every thread.  Every thread loads
 // its kPerThread entries of a chunk at once (no early exit), so a chunk of
-// kPrepThreads * kPerThread entries costs one memory round trip.
-__device__ __forceinline__ int list_length(const int32_t *list, int topk, int *scratch) {
+// kChunk entries costs one memory round trip.  The first chunk's entries are
+// returned in first[] (entry k * kPrepThreads + tid in first[k]), so that a
+// list of at most kChunk entries is read once.
+__device__ __forceinline__ int list_length(const int32_t *list, int topk, int *scratch,
+                                           int (&first)[kPerThread]) {
     const int tid = threadIdx.x;
     int n = topk;
-    for (int p0 = 0; p0 < topk; p0 += kPrepThreads * kPerThread) {
+    for (int p0 = 0; p0 < topk; p0 += kChunk) {
         int v[kPerThread];
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
@@ -40,6 +45,7 @@ __device__ __forceinline__ int list_length(const int32_t *list, int topk, int *s
         for (int k = 0; k < kPerThread; ++k) {
             const int p = p0 + k * kPrepThreads + tid;
             if (v[k] < 0) n = min(n, p);
+            if (p0 == 0) first[k] = v[k];
         }
     }
 #pragma unroll
@@ -54,8 +60,8 @@ __device__ __forceinline__ int list_length(const int32_t *list, int topk, int *s
 
 // One work-group per pseudo-request r = b * s_q + i: lens[r] = n and
 // ids[r][p] = the cache token id of entry p for p < n, 0 for n <= p < tok_per.
-// Per chunk, the list entries are loaded first, then their block-table
-// entries, then the ids are stored: two dependent round trips per chunk.
+// Per chunk, the list entries are loaded (the first chunk's are already in
+// registers), then their block-table entries, then the ids are stored.
 __global__ __launch_bounds__(kPrepThreads) void sparse_ids_kernel(
     const int32_t *__restrict__ indices, const int32_t *__restrict__ block_table,
     int64_t bt_stride, int s_q, int topk, int tok_per, int32_t *__restrict__ lens,
@@ -63,16 +69,17 @@ __global__ __launch_bounds__(kPrepThreads) void sparse_ids_kernel(
     __shared__ int scratch[kPrepThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int32_t *list = indices + (int64_t)r * topk;
-    const int n = list_length(list, topk, scratch);
+    int first[kPerThread];
+    const int n = list_length(list, topk, scratch, first);
     if (tid == 0) lens[r] = n;
     const int32_t *bt = block_table + (int64_t)(r / s_q) * bt_stride;
     int32_t *dst = ids + (int64_t)r * tok_per;
-    for (int p0 = 0; p0 < tok_per; p0 += kPrepThreads * kPerThread) {
+    for (int p0 = 0; p0 < tok_per; p0 += kChunk) {
         int pos[kPerThread], page[kPerThread];
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             const int p = p0 + k * kPrepThreads + tid;
-            pos[k] = p < n ? list[p] : -1;
+            pos[k] = p < n ? (p0 == 0 ? first[k] : list[p]) : -1;
         }
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) page[k] = pos[k] >= 0 ? bt[pos[k] / kPage] : 0;

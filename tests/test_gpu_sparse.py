@@ -70,6 +70,24 @@ def test_sparse_decode_matches_oracle(seqlens, s_q, h_q, topk, fp8):
     compare(out, lse, ref, ref_lse, f"sparse {seqlens} h_q={h_q} topk={topk} fp8={fp8}")
 
 
+@pytest.mark.parametrize("h_q,fp8", [(16, True), (64, False)])
+def test_sparse_lists_longer_than_one_load_chunk(h_q, fp8):
+    # the list-length scan reads 2048 entries per round trip: lists of 2600
+    # entries whose first negative entry lies in the second chunk, in the
+    # first chunk with junk after it in the second, or nowhere
+    rng = np.random.default_rng(68 + h_q)
+    seqlens, topk = [3000, 2700], 2600
+    case = W.make_case(seqlens, 2, h_q, seed=69 + h_q, fp8=fp8, spare_pages=1, poison=True)
+    idx = _lists(seqlens, 2, topk, rng, full=True)
+    for (b, i), n in {(0, 0): 2100, (0, 1): 1500, (1, 0): 2047}.items():
+        idx[b, i, n] = -1
+        idx[b, i, n + 1:] = rng.integers(-5, 10**6, topk - n - 1)  # junk past the first -1
+    out, lse = _run(case, idx)
+    ref, ref_lse = oracle.decode_sparse(case.q, case.cache, case.kind, case.block_table, idx,
+                                        case.scale)
+    compare(out, lse, ref, ref_lse, f"sparse long lists h_q={h_q} fp8={fp8}")
+
+
 @pytest.mark.parametrize("h_q,fp8", [(128, False), (64, True), (16, False), (32, True)])
 def test_sparse_growing_scores_restart(h_q, fp8):
     # RoPE keys scaled up along the sequence and lists in ascending order, so
