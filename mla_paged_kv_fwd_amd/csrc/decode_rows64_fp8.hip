@@ -26,15 +26,15 @@
 //
 // A half-page (32 records, 20992 bytes) lands in LDS as the plain memory
 // image, 21 direct-to-LDS loads of 1 KB each; records past the segment's last
-// token are replaced by that token's record.  With a 656-byte record stride
-// (164 dwords, 36 mod 64 banks) both the 16-byte K reads of 16 tokens and the
-// transposed V reads of 8 tokens hit distinct banks, so no swizzle is needed.
-// (Tokens 16 apart share banks, so 8-byte K reads, served 32 lanes at a time,
-// would conflict two ways.)  Token order: MFMA row m of a 16-token k-step
-// holds token tok16(m) = 8 m3 + 4 m1 + 2 m0 + m2 (m = 8 m3 + 4 m2 + 2 m1 + m0),
-// in the K reads, the score scales and mask, and the V reads and scales
-// alike, so the 32-lane passes of the transposed V reads cover the even and
-// then the odd tokens of a k-step, whose 32-byte pieces sit on disjoint banks.
+// token are replaced by that token's record.  The 656-byte record stride
+// (164 dwords, 36 mod 64 banks) needs no swizzle: the 16-byte K reads (16
+// lanes, so 16 tokens, per pass) hit distinct banks.  Tokens 16 apart share
+// banks, so 8-byte reads, served 32 lanes per pass, must not mix them: MFMA
+// row m of a 16-token k-step holds token tok_of_row(m) = 8 m3 + 4 m1 + 2 m0
+// + m2 (m = 8 m3 + 4 m2 + 2 m1 + m0), in the K reads, the score scales and
+// mask, and the V reads and scales alike, so the two 32-lane passes of a
+// transposed V read cover the even and then the odd tokens of a k-step,
+// whose 8-byte pieces sit on disjoint banks.
 //
 // Token-list mode (sparse decode, kList): each "request" is one query token's
 // list of cache token ids; the score waves stage the ids of half-page t + 3 in
