@@ -472,7 +472,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
         }
         __syncthreads();
         {
-            const int r = tid >> 4, d0 = (tid & 15) * 32;
+            // 16 threads per row; thread j takes dims 4 j + 64 k (k = 0..7),
+            // so the 16 lanes of an LDS pass read 64 consecutive floats of
+            // one wave's row (no bank conflicts) and write 256 consecutive
+            // bytes of the output row
+            const int r = tid >> 4, j = tid & 15;
             float mw[kWaves], mf = -INFINITY;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) {
@@ -489,37 +493,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_rowgroup_kernel(
             const float inv = rf > 0.f ? 1.f / rf : 0.f;
             const float lse_val = lf > 0.f ? (mf + log2f(lf)) * 0.69314718055994530942f : -INFINITY;
             const int orow = row0 + r;
+            const float *xr = X + r * kXStride + 4 * j;
             if (nsplit == 1) {
-                uint16_t *dst = a.out + ((int64_t)b * a.M + orow) * kDV + d0;
+                uint16_t *dst = a.out + ((int64_t)b * a.M + orow) * kDV + 4 * j;
 #pragma unroll
-                for (int d = 0; d < 32; d += 8) {
-                    unsigned pk[4];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-                        for (int v = 0; v < kWaves; ++v) {
-                            v0 += aw[v] * X[(v * kRows + r) * kXStride + d0 + d + e];
-                            v1 += aw[v] * X[(v * kRows + r) * kXStride + d0 + d + e + 1];
-                        }
-                        pk[e / 2] = (unsigned)f32_to_bf16_bits(v0 * inv) |
-                                    ((unsigned)f32_to_bf16_bits(v1 * inv) << 16);
-                    }
-                    *(u32x4 *)(dst + d) = (u32x4){pk[0], pk[1], pk[2], pk[3]};
-                }
-                if ((tid & 15) == 0) a.lse[(int64_t)b * a.M + orow] = lse_val;
-            } else {
-                const int slot = split_base[b] + rank;
-                float *dst = a.o_part + ((int64_t)slot * a.M + orow) * kDV + d0;
-#pragma unroll
-                for (int d = 0; d < 32; d += 4) {
+                for (int k = 0; k < 8; ++k) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int v = 0; v < kWaves; ++v)
-                        acc += aw[v] * *(const f32x4 *)(X + (v * kRows + r) * kXStride + d0 + d);
-                    *(f32x4 *)(dst + d) = acc * inv;
+                        acc += aw[v] * *(const f32x4 *)(xr + v * kRows * kXStride + 64 * k);
+                    acc *= inv;
+                    *(u32x2_t *)(dst + 64 * k) =
+                        (u32x2_t){(unsigned)f32_to_bf16_bits(acc[0]) | ((unsigned)f32_to_bf16_bits(acc[1]) << 16),
+                                  (unsigned)f32_to_bf16_bits(acc[2]) | ((unsigned)f32_to_bf16_bits(acc[3]) << 16)};
                 }
-                if ((tid & 15) == 0) a.lse_part[(int64_t)slot * a.M + orow] = lse_val;
+                if (j == 0) a.lse[(int64_t)b * a.M + orow] = lse_val;
+            } else {
+                const int slot = split_base[b] + rank;
+                float *dst = a.o_part + ((int64_t)slot * a.M + orow) * kDV + 4 * j;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int v = 0; v < kWaves; ++v)
+                        acc += aw[v] * *(const f32x4 *)(xr + v * kRows * kXStride + 64 * k);
+                    *(f32x4 *)(dst + 64 * k) = acc * inv;
+                }
+                if (j == 0) a.lse_part[(int64_t)slot * a.M + orow] = lse_val;
             }
         }
         __syncthreads();  // LDS is reused by the next segment

@@ -21,6 +21,7 @@ constexpr int kXStride = kDV + 4;  // padded row stride of the output stage
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Both halves' maximum for lanes l and l ^ 32.
 __device__ __forceinline__ float max_xor32(float x) {
@@ -101,24 +102,31 @@ __device__ __forceinline__ void stage_first_ids(lds_i32 *ids, const Segment &sg,
 __device__ __forceinline__ void write_rows(const DecodeArgs &a, const Segment &sg,
                                            const int32_t *split_base, const float *X,
                                            const float *row_sum, int row0, int tid) {
-    const int r = tid >> 2, c0 = (tid & 3) * 128;
-    const int orow = row0 + r;
-    if (orow >= a.M) return;
-    const float *xr = X + r * kXStride + c0;
-    const float lsum = row_sum[r];
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    if (sg.nsplit == 1) {
-        uint16_t *dst = a.out + ((int64_t)sg.b * a.M + orow) * kDV + c0;
-#pragma unroll 4
-        for (int d = 0; d < 128; d += 8) {
-            const f32x4 u0 = *(const f32x4 *)(xr + d) * inv, u1 = *(const f32x4 *)(xr + d + 4) * inv;
-            *(u32x4 *)(dst + d) = (u32x4){pack_bf16(u0[0], u0[1]), pack_bf16(u0[2], u0[3]),
-                                          pack_bf16(u1[0], u1[1]), pack_bf16(u1[2], u1[3])};
+    // 16 threads per row, four rounds of 16 rows; thread j of a row takes
+    // dims 4 j + 64 k (k = 0..7), so the 16 lanes of an LDS pass read 64
+    // consecutive floats of one row (no bank conflicts) and write 256
+    // consecutive bytes of it
+    const int j = tid & 15;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * rr + (tid >> 4);
+        const int orow = row0 + r;
+        if (orow >= a.M) continue;
+        const float *xr = X + r * kXStride + 4 * j;
+        const float lsum = row_sum[r];
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        if (sg.nsplit == 1) {
+            uint16_t *dst = a.out + ((int64_t)sg.b * a.M + orow) * kDV + 4 * j;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const f32x4 u = *(const f32x4 *)(xr + 64 * k) * inv;
+                *(u32x2 *)(dst + 64 * k) = (u32x2){pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+            }
+        } else {
+            float *dst = a.o_part + ((int64_t)(split_base[sg.b] + sg.rank) * a.M + orow) * kDV + 4 * j;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) *(f32x4 *)(dst + 64 * k) = *(const f32x4 *)(xr + 64 * k) * inv;
         }
-    } else {
-        float *dst = a.o_part + ((int64_t)(split_base[sg.b] + sg.rank) * a.M + orow) * kDV + c0;
-#pragma unroll 4
-        for (int d = 0; d < 128; d += 4) *(f32x4 *)(dst + d) = *(const f32x4 *)(xr + d) * inv;
     }
 }
 
