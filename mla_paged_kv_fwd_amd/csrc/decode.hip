@@ -16,10 +16,13 @@
 // row (lane % 16).
 //
 // LDS slice layout ("chunk-major", swizzled): 16-byte chunk c of token t of a
-// slice sits in slot c * 16 + (t ^ 4 * (c & 1)).  The K operand of QK^T is
-// then one 1 KB ds_read_b128 block per wave, and the V^T operand of PV a
-// ds_read_b64_tr_b16 (4 tokens x 16 dims transposed per 16-lane group); the
-// XOR keeps both free of bank conflicts.
+// slice sits in slot c * 16 + (t ^ 8 * (c & 1)).  The K operand of QK^T is
+// then one 1 KB ds_read_b128 block per wave (16 lanes, one chunk row of 256
+// contiguous bytes, per pass), and the V^T operand of PV a ds_read_b64_tr_b16
+// (4 tokens x 16 dims transposed per 16-lane group) whose two 16-lane groups
+// of a 32-lane pass read chunks 2 dt and 2 dt + 1: the XOR puts those 128
+// bytes apart, so both reads are free of bank conflicts (with t ^ 4 (c & 1)
+// the V reads conflicted two ways).
 //
 // FP8 cache: the slice holds the raw 656-byte records, chunk c of token t in
 // slot c * 16 + (t ^ 8 * (c & 1)), and both operands are read straight from
@@ -74,8 +77,8 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
     const int lr = lane & 15, lg = lane >> 4;
     if constexpr (!FP8) {
         // block s = chunks 4 s + lg of the slice's tokens; the swizzle puts
-        // token lr ^ 4 (lg & 1) in this lane's slot
-        int t = kSlice * w + (lr ^ (4 * (lg & 1)));
+        // token lr ^ 8 (lg & 1) in this lane's slot
+        int t = kSlice * w + (lr ^ (8 * (lg & 1)));
         t = t < tok_last ? t : tok_last;
         const unsigned char *src = kv + (phys * kPage + t) * kTokBytesBf16 + lg * 16;
 #pragma unroll
@@ -106,7 +109,7 @@ __device__ __forceinline__ void issue_slice(const unsigned char *kv, int64_t phy
 template <bool FP8>
 __device__ __forceinline__ int lane_token(int w, int lane) {
     const int lr = lane & 15, lg = lane >> 4;
-    return kSlice * w + (lr ^ ((FP8 ? 8 : 4) * (lg & 1)));
+    return kSlice * w + (lr ^ (8 * (lg & 1)));
 }
 template <bool FP8>
 __device__ __forceinline__ void issue_rec(const unsigned char *rec, int lane, unsigned lds_dst) {
@@ -124,9 +127,6 @@ __device__ __forceinline__ void issue_rec(const unsigned char *rec, int lane, un
         }
     }
 }
-
-// slot of chunk c of token t in a swizzled bf16 slice
-__device__ __forceinline__ int slot16(int c, int t) { return c * 16 + (t ^ (4 * (c & 1))); }
 
 // byte address of chunk c of token t in a swizzled FP8 slice
 __device__ __forceinline__ int slot8(int c, int t) { return (c * 16 + (t ^ (8 * (c & 1)))) * 16; }
@@ -162,7 +162,7 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
                                              int lane, int tok0, int n_visible, float scale_log2,
                                              const f32x4 *tsc) {
     const int lr = lane & 15, lg = lane >> 4;
-    const int kl = lane ^ (4 * (lg & 1));  // slot of (chunk 4 ks + lg, token lr) in block ks
+    const int kl = lane ^ (8 * (lg & 1));  // slot of (chunk 4 ks + lg, token lr) in block ks
     // S^T (16 tokens x 16 rows) = K (16 x 576) . Q^T (576 x 16).  bf16 cache:
     // two accumulation chains.  FP8 cache: one chain per 128-dim scale tile
     // plus one for the RoPE dims, combined with the token scales afterwards.
@@ -256,7 +256,7 @@ __device__ __forceinline__ void attend_slice(const lds_u8 *S, const bf16x8 *qf, 
     // O^T (512 dims x 16 rows) += V^T (512 x 16 tokens) . P^T (16 tokens x 16 rows)
     if constexpr (!FP8) {
         const int vp = (lr >> 1) & 1;  // chunk parity of this lane's V reads
-        const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ vp) + (lr >> 2)) * 16 + 8 * (lr & 1);
+        const lds_u8 *vt = S + (vp * 16 + 4 * (lg ^ (2 * vp)) + (lr >> 2)) * 16 + 8 * (lr & 1);
 #pragma unroll
         for (int dt = 0; dt < kDV / 16; ++dt) {
             const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
